@@ -1,0 +1,175 @@
+/*
+ * Q8_0 qdot oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU statement of what the Q8_0 block
+ * contraction computes.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this file's library.  The GPU
+ * product never links, loads or calls it, and this file includes no GPU
+ * header and shares no code with the GPU path.
+ *
+ * Sources (Phobos documentation pages):
+ *   - "Phobos Language Spec", section "Quantized built-ins", Q8_0 table,
+ *     row qdot_t: out[i,j] = sum over 32-wide blocks b of
+ *     a_scales[i,b] * w_scales[j,b] * (sum over k in b of a[i,k] * w[j,k]);
+ *     scales are [M, K/32] and [N, K/32].
+ *   - "Quantized built-ins and formats", section "Q8_0": signed bytes with
+ *     one scale per block of 32 values; activations are quantized the same
+ *     way; the inner sum is taken in integers (four bytes at a time with
+ *     dp4a on the pages' hardware).
+ *   - "Phobos Language Spec", section "Types": i8 loads sign-extend.
+ *
+ * Readings where the pages are silent:
+ *   - The quantizer (the pages never say how Q8_0 values are produced):
+ *     per 32-block, amax = max |x|, d = f32(amax / 127),
+ *     q = clamp(round-half-even(x / d), -127, 127) computed in f32, and
+ *     d == 0 gives q == 0.  Ties-to-even matches the spec's round()
+ *     ("Phobos Language Spec", section "Elementwise").
+ *   - Accumulation across blocks is done here in f64, in block order;
+ *     AS*WS is exact in f64 (24 + 24 mantissa bits).
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -shared -fPIC.
+ * No -ffast-math and no -march: the f32 quantizer must use IEEE division
+ * and round-to-nearest-even exactly as written.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define Q8_BLOCK 32
+
+/* Number of threads the OpenMP loops below use (1 without OpenMP). */
+int q8o_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Q8_0 quantization of `rows` f32 rows of length K (K a multiple of 32).
+ * q: int8 [rows][K]; d: f32 [rows][K/32].  Returns 0, or -1 for a bad K.
+ */
+int q8o_quantize_rows(const float *x, int64_t rows, int64_t K,
+                      int8_t *q, float *d) {
+    if (K <= 0 || K % Q8_BLOCK != 0 || rows < 0) return -1;
+    const int64_t KB = K / Q8_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < KB; ++b) {
+            const float *xb = x + r * K + b * Q8_BLOCK;
+            int8_t *qb = q + r * K + b * Q8_BLOCK;
+            float amax = 0.0f;
+            for (int t = 0; t < Q8_BLOCK; ++t) {
+                float a = fabsf(xb[t]);
+                if (a > amax) amax = a;
+            }
+            float scale = amax / 127.0f; /* one f32 division, rounded to nearest */
+            d[r * KB + b] = scale;
+            for (int t = 0; t < Q8_BLOCK; ++t) {
+                if (scale == 0.0f) {
+                    qb[t] = 0;
+                    continue;
+                }
+                float v = rintf(xb[t] / scale); /* f32 division, then ties-to-even */
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+                qb[t] = (int8_t)v;
+            }
+        }
+    }
+    return 0;
+}
+
+/* One block's integer dot: sum over t < 32 of i32(a[t]) * i32(w[t]). */
+static int32_t block_dot(const int8_t *a, const int8_t *w) {
+    int32_t s = 0;
+    for (int t = 0; t < Q8_BLOCK; ++t) s += (int32_t)a[t] * (int32_t)w[t];
+    return s;
+}
+
+/*
+ * Per-block integer partials P[i][j][b] (int32, row-major [M][N][K/32]).
+ * |P| <= 32 * 128 * 128 = 2^19, so int32 is exact.
+ */
+int q8o_block_partials(const int8_t *A, const int8_t *W, int32_t *P,
+                       int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K <= 0 || K % Q8_BLOCK != 0) return -1;
+    const int64_t KB = K / Q8_BLOCK;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            for (int64_t b = 0; b < KB; ++b)
+                P[(i * N + j) * KB + b] =
+                    block_dot(A + i * K + b * Q8_BLOCK, W + j * K + b * Q8_BLOCK);
+    return 0;
+}
+
+/* One output: the definition in f64, plus the sum of |terms|. */
+static void qdot_one(const int8_t *A, const float *AS, const int8_t *W,
+                     const float *WS, int64_t i, int64_t j, int64_t K,
+                     double *out, double *abs_terms) {
+    const int64_t KB = K / Q8_BLOCK;
+    double acc = 0.0, mag = 0.0;
+    for (int64_t b = 0; b < KB; ++b) {
+        int32_t p = block_dot(A + i * K + b * Q8_BLOCK, W + j * K + b * Q8_BLOCK);
+        double s = (double)AS[i * KB + b] * (double)WS[j * KB + b]; /* exact */
+        double term = s * (double)p;
+        acc += term;
+        mag += fabs(term);
+    }
+    *out = acc;
+    *abs_terms = mag;
+}
+
+/*
+ * out[i][j] = sum_b AS[i,b] * WS[j,b] * P[i,j,b] in f64, in block order;
+ * abs_terms[i][j] = sum_b |AS[i,b] * WS[j,b] * P[i,j,b]|.
+ * A int8 [M][K], AS f32 [M][K/32], W int8 [N][K], WS f32 [N][K/32].
+ */
+int q8o_qdot_f64(const int8_t *A, const float *AS, const int8_t *W,
+                 const float *WS, int64_t M, int64_t N, int64_t K,
+                 double *out, double *abs_terms) {
+    if (M < 0 || N < 0 || K <= 0 || K % Q8_BLOCK != 0) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            qdot_one(A, AS, W, WS, i, j, K, out + i * N + j, abs_terms + i * N + j);
+    return 0;
+}
+
+/*
+ * The same definition at `count` sampled output positions (ii[s], jj[s]),
+ * for checks at sizes where the whole output would be too slow here.
+ */
+int q8o_qdot_f64_at(const int8_t *A, const float *AS, const int8_t *W,
+                    const float *WS, int64_t M, int64_t N, int64_t K,
+                    const int64_t *ii, const int64_t *jj, int64_t count,
+                    double *out, double *abs_terms) {
+    if (M < 0 || N < 0 || K <= 0 || K % Q8_BLOCK != 0 || count < 0) return -1;
+    for (int64_t s = 0; s < count; ++s)
+        if (ii[s] < 0 || ii[s] >= M || jj[s] < 0 || jj[s] >= N) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < count; ++s)
+        qdot_one(A, AS, W, WS, ii[s], jj[s], K, out + s, abs_terms + s);
+    return 0;
+}
+
+/* Partials P[s][b] for sampled (ii[s], jj[s]) positions: int32 [count][K/32]. */
+int q8o_block_partials_at(const int8_t *A, const int8_t *W, int64_t M, int64_t N,
+                          int64_t K, const int64_t *ii, const int64_t *jj,
+                          int64_t count, int32_t *P) {
+    if (M < 0 || N < 0 || K <= 0 || K % Q8_BLOCK != 0 || count < 0) return -1;
+    for (int64_t s = 0; s < count; ++s)
+        if (ii[s] < 0 || ii[s] >= M || jj[s] < 0 || jj[s] >= N) return -2;
+    const int64_t KB = K / Q8_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < count; ++s)
+        for (int64_t b = 0; b < KB; ++b)
+            P[s * KB + b] = block_dot(A + ii[s] * K + b * Q8_BLOCK,
+                                      W + jj[s] * K + b * Q8_BLOCK);
+    return 0;
+}
