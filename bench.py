@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q8_0 block contraction on one MI355X.
+
+One step = one ``q8_qdot`` call (the whole path: Q8_0 operands -> int32 block
+sums -> f32 block-scale epilogue -> C) on the decode workload M=1, N=14336,
+K=4096 (FFN up-projection shape).  Inputs are seeded synthetic f32 drawn by
+``synth`` and quantized on the GPU by the library's own ``q8_quantize``; R
+distinct device copies of every operand are rotated so that no launch finds
+its operands in the 256 MB last-level cache or the L2s: each step reads its
+weights from HBM, as a decode step would.
+
+Printed: one JSON line with the headline metric (weight GB/s of the M=1
+matvec), the roofline of the dominant kernel (HBM), the batched M=512 qGEMM
+as a second measured workload (int8 TOPS, MFMA and VALU rooflines), and the
+CPU oracle timed on this host on a bounded sample of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POP/s)
+# VALU lane-op rate with packed-FP32 forms off: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz.
+VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
+EPILOGUE_VALU_OPS = 2            # f32 VALU ops per (i, j, block) in the MFMA epilogue
+CACHE_DEFEAT_BYTES = 1 << 30     # rotate >= 1 GiB of distinct operand copies
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS for the headline")
+    ap.add_argument("--second", type=int, default=4, help="second measured workload (-1: none)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
+    ap.add_argument("--no-rotate", action="store_true", help="reuse one copy (cache-warm number)")
+    return ap.parse_args()
+
+
+class Operands:
+    """R device copies of (A, AS, W, WS, C) for one workload, quantized on the GPU."""
+
+    def __init__(self, torch, q8, w: synth.Workload, rotate: bool):
+        self.w = w
+        dev = torch.device("cuda:0")
+        a32, w32 = synth.workload_f32(w)
+        Xa = torch.from_numpy(a32).to(dev)
+        Xw = torch.from_numpy(w32).to(dev)
+        A, AS = q8.q8_quantize(Xa)
+        W, WS = q8.q8_quantize(Xw)
+        del Xa, Xw
+        per_copy = A.numel() + AS.numel() * 4 + W.numel() + WS.numel() * 4 + w.M * w.N * 4
+        self.R = max(1, -(-CACHE_DEFEAT_BYTES // per_copy)) if rotate else 1
+        self.copies = []
+        for r in range(self.R):
+            if r == 0:
+                cA, cAS, cW, cWS = A, AS, W, WS
+            else:
+                cA, cAS, cW, cWS = A.clone(), AS.clone(), W.clone(), WS.clone()
+            C = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+            self.copies.append((cA, cAS, cW, cWS, C))
+        torch.cuda.synchronize()
+        self.weight_bytes = W.numel() + WS.numel() * 4
+        self.act_bytes = A.numel() + AS.numel() * 4
+        self.out_bytes = w.M * w.N * 4
+        self.algo_bytes = self.weight_bytes + self.act_bytes + self.out_bytes
+        self.int8_ops = 2 * w.M * w.N * w.K
+        self.element_blocks = w.M * w.N * w.KB
+
+
+def time_launches(torch, q8, ops: Operands, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` launches between two HIP events."""
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    cps = ops.copies
+    w = ops.w
+    raw = q8.q8_qdot_raw
+    ptrs = [(a.data_ptr(), s.data_ptr(), b.data_ptr(), t.data_ptr(), c.data_ptr()) for a, s, b, t, c in cps]
+    for k in range(warmup):
+        st = raw(*ptrs[k % len(ptrs)], w.M, w.N, w.K, sptr)
+        if st:
+            raise RuntimeError("q8_qdot failed: %s" % q8.q8_strerror(st))
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for k in range(steps):
+        raw(*ptrs[k % len(ptrs)], w.M, w.N, w.K, sptr)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    return ms / steps, wall
+
+
+def cpu_baseline(ops_w: synth.Workload, budget_s: float):
+    """The oracle as it stands, on this host, on a bounded sample of the workload."""
+    import oracle
+    a32, w32 = synth.workload_f32(ops_w)
+    A, AS = oracle.quantize_rows(a32)
+    W, WS = oracle.quantize_rows(w32)
+    del a32, w32
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.qdot_f64(A, AS, W, WS)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 3 and time.perf_counter() - t_all >= budget_s:
+            break
+        if len(times) >= 1000:
+            break
+    per = statistics.median(times)
+    wbytes = W.nbytes + WS.nbytes
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": round(wbytes / per / 1e9, 3),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d full passes of %s (M=%d N=%d K=%d), median %.1f ms each, %.1f s total; "
+                  "host %s, %d CPUs in affinity"
+                  % (len(times), ops_w.name, ops_w.M, ops_w.N, ops_w.K, per * 1e3,
+                     sum(times), cpu_model or platform.processor(), len(os.sched_getaffinity(0))),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(--gpus %d requested)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_q8_qdot_amd as q8
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a visible gfx950 GPU", file=sys.stderr)
+        sys.exit(1)
+    q8.ensure_built()
+    q8.load()
+
+    head_w = synth.WORKLOADS[args.workload]
+    log("[bench] preparing %s" % head_w.name)
+    head = Operands(torch, q8, head_w, rotate=not args.no_rotate)
+    log("[bench] %s: %d rotated copies; timing %d steps after %d warmup"
+        % (head_w.name, head.R, args.steps, args.warmup))
+    ms, wall = time_launches(torch, q8, head, args.steps, args.warmup)
+    achieved = head.algo_bytes / (ms * 1e-3) / 1e9
+    weight_gbs = head.weight_bytes / (ms * 1e-3) / 1e9
+    path = q8.q8_qdot_path(head_w.M, head_w.N, head_w.K)
+    dtype = "i8xi8->i32, f32 scales"
+    result = {
+        "metric": "Q8_0 matvec weight GB/s (M=1)",
+        "value": round(weight_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations, Q8_0-quantized on GPU)",
+        "config": {"workload": head_w.name, "M": head_w.M, "N": head_w.N, "K": head_w.K,
+                   "kernel": "matvec" if path == 0 else "qgemm",
+                   "rotated_copies": head.R, "arith": dtype},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": head.algo_bytes,
+                     "kernel_us": round(ms * 1e3, 3)},
+    }
+    log("[bench] headline %.3f us/launch, %.1f GB/s weights, %.1f GB/s total (%.1f%% of HBM)"
+        % (ms * 1e3, weight_gbs, achieved, 100 * achieved / HBM_PEAK_GBS))
+    del head
+    torch.cuda.empty_cache()
+
+    if args.second >= 0:
+        sw = synth.WORKLOADS[args.second]
+        log("[bench] preparing %s" % sw.name)
+        sec = Operands(torch, q8, sw, rotate=not args.no_rotate)
+        steps2 = max(10, args.steps // 4)
+        ms2, _ = time_launches(torch, q8, sec, steps2, max(3, args.warmup // 4))
+        tops = sec.int8_ops / (ms2 * 1e-3) / 1e12
+        valu_floor_us = sec.element_blocks * EPILOGUE_VALU_OPS / VALU_LANE_OPS_PER_S * 1e6
+        hbm_gbs = sec.algo_bytes / (ms2 * 1e-3) / 1e9
+        result["second"] = {
+            "workload": sw.name, "M": sw.M, "N": sw.N, "K": sw.K, "steps": steps2,
+            "us_per_launch": round(ms2 * 1e3, 3),
+            "int8_tops": round(tops, 2),
+            "roofline_mfma": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
+                              "unit": "TOPS", "frac": round(tops / INT8_PEAK_TOPS, 4)},
+            "valu_epilogue_floor_us": round(valu_floor_us, 2),
+            "valu_floor_frac": round(valu_floor_us / (ms2 * 1e3), 4),
+            "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+            "rotated_copies": sec.R,
+        }
+        log("[bench] second %s: %.3f us/launch, %.1f int8 TOPS (%.1f%% of peak), VALU floor %.1f us"
+            % (sw.name, ms2 * 1e3, tops, 100 * tops / INT8_PEAK_TOPS, valu_floor_us))
+        del sec
+        torch.cuda.empty_cache()
+
+    if args.cpu_seconds > 0:
+        log("[bench] CPU oracle baseline (~%.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(head_w, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+// Q8_0 matvec for small M (decode step): C[i, :] = qdot_t(A[i, :], AS[i, :], W, WS).
+//
+// What is computed: the qdot_t row of the Q8_0 table ("Phobos Language Spec",
+// section "Quantized built-ins"), with the inner block sum in integers as the
+// "Quantized built-ins and formats" page's Q8_0 section describes, and the
+// weights read at their stored size (that page's introduction: raw block bytes
+// are decoded in registers, so weights cross the memory bus at 1 byte per
+// value plus the block scale).
+//
+// Prior art on the pages: the q8_qdot decode kernel (one activation row
+// against 64 output columns per CTA, Q8_0 section) and lanes_matvec (one warp
+// per row, lane-strided 4-element runs, a lane fold; "Uniform, warp-uniform
+// and varying").  Design here, for CDNA4 wave64:
+//   - a wave owns R weight rows at a time and walks rows with a grid stride;
+//   - lane l reads bytes [1024 s + 16 l, +16) of a row: each load instruction
+//     covers 1 KiB of contiguous weight bytes, so W streams fully coalesced;
+//   - lanes 2m and 2m+1 hold the two halves of block (1024 s)/32 + m: each
+//     lane does 4 v_dot4_i32_i8, one DPP swap adds the partner's half, giving
+//     the exact int32 block sum in both lanes;
+//   - the activation row and its scales stay in VGPRs for the whole kernel
+//     when K <= 16 KiB (else they are re-read per chunk); the activation scale
+//     is zeroed in odd lanes so each block is scaled and accumulated once;
+//   - the f32 accumulator is folded across the wave with DPP (no LDS).
+// HBM-bound: algorithmic traffic is N*K weight bytes + N*K/8 scale bytes.
+#include "q8_device.h"
+#include "q8_launch.h"
+
+namespace q8 {
+namespace {
+
+constexpr int kStepBytes = kWave * 16;  // one 16-byte load per lane = 1 KiB of a row
+constexpr int kMatvecThreads = 256;     // 4 waves per workgroup
+constexpr int kMaxSteps = 16;           // activation row resident in VGPRs up to K = 16 KiB
+constexpr int kMatvecMaxWaves = 256 * 16;
+
+template <int S, int R, bool PARTIALS>
+__global__ void __launch_bounds__(kMatvecThreads)
+matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
+              const int8_t* __restrict__ W, const float* __restrict__ WS,
+              float* __restrict__ C, int32_t* __restrict__ P, int N, int K) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int waves_per_wg = kMatvecThreads / kWave;
+    const int wave = blockIdx.x * waves_per_wg + (threadIdx.x / kWave);
+    const int nwaves = gridDim.x * waves_per_wg;
+    const int i = blockIdx.y;
+    const int KB = K / kBlock;
+    const int chunk = S * kStepBytes;
+    const int nchunks = (K + chunk - 1) / chunk;
+    const int groups = (N + R - 1) / R;
+    const bool even = (lane & 1) == 0;
+    const int8_t* Ai = A + (int64_t)i * K;
+
+    v4i a[S];
+    float as[S];
+    auto load_a = [&](int c) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int off = c * chunk + s * kStepBytes + lane * 16;
+            const bool ok = off < K;
+            a[s] = ok ? load16(Ai + off) : v4i{0, 0, 0, 0};
+            if constexpr (!PARTIALS)
+                as[s] = (ok && even) ? AS[(int64_t)i * KB + off / kBlock] : 0.0f;
+        }
+    };
+    if (nchunks == 1) load_a(0);
+
+    for (int g = wave; g < groups; g += nwaves) {
+        const int j0 = g * R;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+        for (int c = 0; c < nchunks; ++c) {
+            if (nchunks > 1) load_a(c);
+            v4i w[R][S];
+            float ws[R][S];
+            // Issue every load of the row group before the first use.
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int j = j0 + r;
+                const bool row_ok = j < N;
+                const int8_t* Wj = W + (int64_t)j * K;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const int off = c * chunk + s * kStepBytes + lane * 16;
+                    const bool ok = row_ok && off < K;
+                    w[r][s] = ok ? load16_stream(Wj + off) : v4i{0, 0, 0, 0};
+                    if constexpr (!PARTIALS)
+                        ws[r][s] = ok ? WS[(int64_t)j * KB + off / kBlock] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int j = j0 + r;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    int p = dot16(a[s], w[r][s], 0);
+                    p += dpp_i32<kDppSwapPairs>(p);  // exact block sum in both lanes of the pair
+                    if constexpr (PARTIALS) {
+                        const int off = c * chunk + s * kStepBytes + lane * 16;
+                        if (even && j < N && off < K)
+                            P[((int64_t)i * N + j) * KB + off / kBlock] = p;
+                    } else {
+                        acc[r] = fmaf(as[s] * ws[r][s], (float)p, acc[r]);
+                    }
+                }
+            }
+        }
+        if constexpr (!PARTIALS) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float tot = wave_sum(acc[r]);
+                if (lane == 0 && j0 + r < N) C[(int64_t)i * N + j0 + r] = tot;
+            }
+        }
+    }
+}
+
+template <int S, bool PARTIALS>
+hipError_t launch_s(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                    float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    // Rows per wave: about 16 x 16-byte weight loads in flight per lane.
+    constexpr int R = S <= 2 ? 8 : (S <= 4 ? 4 : (S <= 8 ? 2 : 1));
+    const int groups = (N + R - 1) / R;
+    const int waves = groups < kMatvecMaxWaves ? groups : kMatvecMaxWaves;
+    const int wgs = (waves + kMatvecThreads / kWave - 1) / (kMatvecThreads / kWave);
+    dim3 grid(wgs, M);
+    matvec_kernel<S, R, PARTIALS><<<grid, kMatvecThreads, 0, stream>>>(A, AS, W, WS, C, P, N, K);
+    return hipGetLastError();
+}
+
+template <bool PARTIALS>
+hipError_t launch_any(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                      float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    int steps = (K + kStepBytes - 1) / kStepBytes;
+    if (steps > kMaxSteps) steps = kMaxSteps;
+    switch (steps) {
+#define Q8_MATVEC_CASE(S_) \
+    case S_: return launch_s<S_, PARTIALS>(A, AS, W, WS, C, P, M, N, K, stream);
+        Q8_MATVEC_CASE(1) Q8_MATVEC_CASE(2) Q8_MATVEC_CASE(3) Q8_MATVEC_CASE(4)
+        Q8_MATVEC_CASE(5) Q8_MATVEC_CASE(6) Q8_MATVEC_CASE(7) Q8_MATVEC_CASE(8)
+        Q8_MATVEC_CASE(9) Q8_MATVEC_CASE(10) Q8_MATVEC_CASE(11) Q8_MATVEC_CASE(12)
+        Q8_MATVEC_CASE(13) Q8_MATVEC_CASE(14) Q8_MATVEC_CASE(15) Q8_MATVEC_CASE(16)
+#undef Q8_MATVEC_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    if (P != nullptr) return launch_any<true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_any<false>(A, AS, W, WS, C, P, M, N, K, stream);
+}
+
+}  // namespace q8

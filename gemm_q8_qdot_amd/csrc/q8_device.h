@@ -1,0 +1,70 @@
+// Device-side helpers shared by the Q8_0 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+constexpr int kBlock = 32;   // Q8_0 block: 32 consecutive k share one scale
+constexpr int kWave = 64;    // CDNA wavefront width
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppSwapPairs = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppSwapHalves = 0x4E;  // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowHalfMirror = 0x141;  // lane k <- 7 - k within 8 lanes
+constexpr int kDppRowMirror = 0x140;      // lane k <- 15 - k within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Signed 4 x i8 dot product accumulated into an int32 (v_dot4_i32_i8): the
+// "Phobos Language Spec" dp4a of section "Operators and conversions" -- acc
+// plus the sum of the products of the four signed bytes of x and of y.
+__device__ __forceinline__ int dot4(int x, int y, int acc) {
+    return __builtin_amdgcn_sdot4(x, y, acc, false);
+}
+
+// Integer dot of 16 signed bytes.
+__device__ __forceinline__ int dot16(v4i a, v4i w, int acc) {
+    acc = dot4(a.x, w.x, acc);
+    acc = dot4(a.y, w.y, acc);
+    acc = dot4(a.z, w.z, acc);
+    acc = dot4(a.w, w.w, acc);
+    return acc;
+}
+
+// Sum over all 64 lanes; every lane gets the total.  Fixed order, so the
+// result is deterministic: two DPP quad steps, two DPP mirror steps (each
+// 16-lane row then holds its row sum), then the four row sums via readlane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f32<kDppSwapPairs>(v);
+    v += dpp_f32<kDppSwapHalves>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    v += dpp_f32<kDppRowMirror>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ v4i load16(const int8_t* p) {
+    return *reinterpret_cast<const v4i*>(p);
+}
+
+__device__ __forceinline__ v4i load16_stream(const int8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
+
+}  // namespace q8

@@ -1,0 +1,29 @@
+// Host-side launch helpers behind the C-ABI (internal; not exported).
+// Arguments are validated by the caller (q8qdot_api.cpp): non-negative
+// shapes, K % 32 == 0, aligned non-null pointers.  Each helper only enqueues
+// kernels on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+// M < 8: wave64 matvec, one activation row per grid row (blockIdx.y).
+// P == nullptr -> f32 output C; otherwise int32 partials P, C unused.
+hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream);
+
+// M >= 8: int8-MFMA block GEMM.  Same P convention.
+hipError_t launch_qgemm(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream);
+
+// Q8_0 quantization of f32 rows.
+hipError_t launch_quantize(const float* X, int8_t* Q, float* D, int rows, int K,
+                           hipStream_t stream);
+
+// C[0 .. count) = 0.0f with a plain fill kernel (no memset node, so the
+// call stays safe inside a captured graph).
+hipError_t launch_fill_zero(float* C, int64_t count, hipStream_t stream);
+
+}  // namespace q8

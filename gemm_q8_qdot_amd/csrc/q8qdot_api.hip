@@ -1,0 +1,114 @@
+// C-ABI of the Q8_0 contraction library: host-side validation and dispatch.
+// Declarations and the contract of every entry point: include/q8qdot.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/q8qdot.h"
+#include "q8_launch.h"
+
+#define Q8_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kMatvecMaxM = 7;  // M < 8 -> matvec; the MFMA path needs 8+ rows to pay off
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(int M, int N, int K) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return Q8_EINVAL;
+    return Q8_OK;
+}
+
+// Largest element offset any kernel forms must fit in int64 bytes.
+int check_range(int64_t M, int64_t N, int64_t K, bool partials) {
+    const int64_t lim = INT64_MAX / 8;
+    if (M > 0 && K > lim / M) return Q8_ERANGE;
+    if (N > 0 && K > lim / N) return Q8_ERANGE;
+    if (M > 0 && N > lim / M) return Q8_ERANGE;
+    if (partials && M > 0 && N > 0 && K / 32 > lim / (M * N)) return Q8_ERANGE;
+    return Q8_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ELAUNCH; }
+
+int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS, float* C,
+             int32_t* P, int M, int N, int K, hipStream_t stream) {
+    int st = check_shape(M, N, K);
+    if (st != Q8_OK) return st;
+    st = check_range(M, N, K, P != nullptr);
+    if (st != Q8_OK) return st;
+    if (M == 0 || N == 0) return Q8_OK;  // empty output
+    const bool partials = P != nullptr;
+    if (K == 0) {
+        // Empty sum over blocks: C = 0; P has no elements.
+        if (partials) return Q8_OK;
+        if (C == nullptr) return Q8_ENULL;
+        if (!aligned(C, 4)) return Q8_EALIGN;
+        return status_of(q8::launch_fill_zero(C, (int64_t)M * N, stream));
+    }
+    if (A == nullptr || W == nullptr) return Q8_ENULL;
+    if (!partials && (AS == nullptr || WS == nullptr || C == nullptr)) return Q8_ENULL;
+    if (!aligned(A, 16) || !aligned(W, 16)) return Q8_EALIGN;
+    if (partials) {
+        if (!aligned(P, 4)) return Q8_EALIGN;
+    } else if (!aligned(AS, 4) || !aligned(WS, 4) || !aligned(C, 4)) {
+        return Q8_EALIGN;
+    }
+    hipError_t e = M <= kMatvecMaxM
+                       ? q8::launch_matvec(A, AS, W, WS, C, P, M, N, K, stream)
+                       : q8::launch_qgemm(A, AS, W, WS, C, P, M, N, K, stream);
+    return status_of(e);
+}
+
+}  // namespace
+
+Q8_API int q8_qdot_stream(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                          float* C, int M, int N, int K, void* stream) {
+    return run_qdot(A, AS, W, WS, C, nullptr, M, N, K, static_cast<hipStream_t>(stream));
+}
+
+Q8_API int q8_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                   float* C, int M, int N, int K) {
+    return run_qdot(A, AS, W, WS, C, nullptr, M, N, K, nullptr);
+}
+
+Q8_API int q8_qdot_partials(const int8_t* A, const int8_t* W, int32_t* P, int M, int N, int K,
+                            void* stream) {
+    if (P == nullptr) {
+        int st = check_shape(M, N, K);
+        if (st != Q8_OK) return st;
+        if (M == 0 || N == 0 || K == 0) return Q8_OK;
+        return Q8_ENULL;
+    }
+    return run_qdot(A, nullptr, W, nullptr, nullptr, P, M, N, K, static_cast<hipStream_t>(stream));
+}
+
+Q8_API int q8_qdot_path(int M, int N, int K) {
+    int st = check_shape(M, N, K);
+    if (st != Q8_OK) return st;
+    return M <= kMatvecMaxM ? 0 : 1;
+}
+
+Q8_API int q8_quantize(const float* X, int8_t* Q, float* D, int rows, int K, void* stream) {
+    if (rows < 0 || K < 0 || K % 32 != 0) return Q8_EINVAL;
+    if (rows > 0 && K > INT64_MAX / 8 / rows) return Q8_ERANGE;
+    if (rows == 0 || K == 0) return Q8_OK;
+    if (X == nullptr || Q == nullptr || D == nullptr) return Q8_ENULL;
+    if (!aligned(X, 16) || !aligned(Q, 16) || !aligned(D, 4)) return Q8_EALIGN;
+    return status_of(q8::launch_quantize(X, Q, D, rows, K, static_cast<hipStream_t>(stream)));
+}
+
+Q8_API const char* q8_strerror(int status) {
+    switch (status) {
+        case Q8_OK: return "ok";
+        case Q8_EINVAL: return "invalid shape: M, N, K must be >= 0 and K a multiple of 32";
+        case Q8_ENULL: return "null pointer for an operand the call must dereference";
+        case Q8_EALIGN: return "misaligned pointer: A, W, X, Q need 16 bytes, f32/int32 arrays 4";
+        case Q8_ERANGE: return "extent product overflows 64-bit addressing";
+        case Q8_ELAUNCH: return "HIP runtime rejected the kernel launch";
+        default: return "unknown status";
+    }
+}
+
+Q8_API int q8_version(void) { return kVersion; }

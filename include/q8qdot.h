@@ -1,0 +1,115 @@
+/*
+ * q8qdot -- Q8_0 block-quantized contraction on AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Phobos Language Spec", section "Quantized built-ins",
+ * Q8_0 table, row qdot_t; restated in "Quantized built-ins and formats",
+ * section "Q8_0"):
+ *
+ *     C[i, j] = sum over blocks b of  AS[i, b] * WS[j, b] * P[i, j, b]
+ *     P[i, j, b] = sum over t < 32 of  A[i, 32 b + t] * W[j, 32 b + t]
+ *
+ * with A, W signed bytes (sign-extended, "Phobos Language Spec", section
+ * "Types"), AS, WS f32 block scales, one per 32 consecutive k, and the inner
+ * block sum exact in int32 (|P| <= 32 * 128^2 = 2^19).
+ *
+ * Operand layout (row-major, densely packed, as the "Kernel ABI" page's
+ * section "Memory layout and alignment" requires of every tensor):
+ *
+ *     A   int8  [M][K]        activations, Q8_0 bytes
+ *     AS  f32   [M][K/32]     activation block scales
+ *     W   int8  [N][K]        weights, Q8_0 bytes
+ *     WS  f32   [N][K/32]     weight block scales (same orientation as AS,
+ *                             the qdot_t form; not the transposed qmma_t form)
+ *     C   f32   [M][N]        output, assigned (never read, never accumulated)
+ *     P   int32 [M][N][K/32]  per-block integer partials (debug entry)
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates nothing, keeps no per-call state, never synchronizes and
+ *     never reads an output.  Work is enqueued on `stream` (a hipStream_t;
+ *     NULL means the null stream) and is asynchronous like a kernel launch.
+ *   - Shapes: M, N, K >= 0 and K % 32 == 0.  M or N == 0 is an empty
+ *     output: OK, nothing is launched and pointers are not inspected.
+ *     K == 0 with M, N > 0 is the empty sum: C is filled with 0.0f and A,
+ *     AS, W, WS may be NULL.  M and N need not be multiples of any tile:
+ *     ragged edges are masked inside the kernels (the pages instead ask for
+ *     whole tiles, "Kernel ABI", section "Entry checks").
+ *   - Alignment: A, W (and Q of q8_quantize) must be 16-byte aligned, so
+ *     every row (a multiple of 32 bytes long) can be read with 16-byte
+ *     loads; the f32/int32 arrays must be 4-byte aligned.
+ *   - Errors are detected on the host and returned BEFORE anything is
+ *     enqueued (the pages instead trap at kernel entry and leave the context
+ *     unusable, "Kernel ABI", section "Entry checks").  A size larger than a
+ *     buffer cannot be detected and reads or writes past it, as on the pages.
+ *     A fault inside a kernel surfaces at the caller's next synchronize.
+ *   - Calls are reentrant; calls on different streams may overlap.
+ */
+#ifndef Q8QDOT_H
+#define Q8QDOT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q8_OK = 0,
+    Q8_EINVAL = -1,  /* M, N or K negative, or K % 32 != 0 */
+    Q8_ENULL = -2,   /* a pointer the call must dereference is NULL */
+    Q8_EALIGN = -3,  /* A/W/X/Q not 16-byte aligned, or another array not 4-byte aligned */
+    Q8_ERANGE = -4,  /* an extent product overflows 64-bit byte addressing */
+    Q8_ELAUNCH = -5  /* the HIP runtime rejected the launch (hipGetLastError) */
+} q8_status;
+
+/*
+ * C = qdot_t(A, AS, W, WS) on the null stream.  Dispatches on M like
+ * q8_qdot_path.  Returns a q8_status.
+ */
+int q8_qdot(const int8_t *A, const float *AS, const int8_t *W, const float *WS,
+            float *C, int M, int N, int K);
+
+/* The same on an explicit HIP stream (hipStream_t passed as void*). */
+int q8_qdot_stream(const int8_t *A, const float *AS, const int8_t *W, const float *WS,
+                   float *C, int M, int N, int K, void *stream);
+
+/*
+ * Debug entry: P[i][j][b] = the int32 block sum of the qdot_t definition,
+ * int32 [M][N][K/32] row-major.  Runs the same kernel and the same load and
+ * integer-dot code as q8_qdot for this (M, N, K), stopping before the f32
+ * block-scale epilogue, so each kernel's integer core can be checked bit for
+ * bit.  K == 0 is an empty P: OK, nothing is launched.
+ */
+int q8_qdot_partials(const int8_t *A, const int8_t *W, int32_t *P,
+                     int M, int N, int K, void *stream);
+
+/*
+ * The kernel a shape dispatches to: 0 = wave64 matvec (M < 8; one A row per
+ * grid row), 1 = int8-MFMA block GEMM (M >= 8).  Q8_EINVAL for bad shapes.
+ */
+int q8_qdot_path(int M, int N, int K);
+
+/*
+ * Q8_0 quantization of f32 rows on the GPU (the step that produces A and AS
+ * from an f32 activation; "Quantized built-ins and formats", section "Q8_0":
+ * activations are quantized like the weights, one scale per 32 values).
+ * X f32 [rows][K] -> Q int8 [rows][K], D f32 [rows][K/32].  Per block:
+ * d = f32(max|x| / 127), q = clamp(round-half-even(x / d), -127, 127) with an
+ * IEEE f32 division, and d == 0 gives q == 0.  (The scale and rounding rule
+ * are a reading: the pages do not state how Q8_0 values are produced.)
+ * Inputs must be finite.  rows == 0 or K == 0 is OK (nothing launched).
+ * X and Q must be 16-byte aligned (16-byte loads of X), D 4-byte aligned.
+ */
+int q8_quantize(const float *X, int8_t *Q, float *D, int rows, int K, void *stream);
+
+/* Static text for a q8_status value ("unknown status" otherwise). */
+const char *q8_strerror(int status);
+
+/* Library version, MAJOR * 10000 + MINOR * 100 + PATCH. */
+int q8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8QDOT_H */

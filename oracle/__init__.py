@@ -122,8 +122,8 @@ def _check_ops(A, W):
     W = _c(W, np.int8)
     if A.ndim != 2 or W.ndim != 2 or A.shape[1] != W.shape[1]:
         raise ValueError("A [M,K] and W [N,K] must share K")
-    if A.shape[1] % BLOCK or A.shape[1] == 0:
-        raise ValueError("K must be a positive multiple of 32")
+    if A.shape[1] % BLOCK:
+        raise ValueError("K must be a multiple of 32")
     return A, W
 
 

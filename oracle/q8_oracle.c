@@ -50,12 +50,12 @@ int q8o_num_threads(void) {
 }
 
 /*
- * Q8_0 quantization of `rows` f32 rows of length K (K a multiple of 32).
+ * Q8_0 quantization of `rows` f32 rows of length K (K >= 0, a multiple of 32).
  * q: int8 [rows][K]; d: f32 [rows][K/32].  Returns 0, or -1 for a bad K.
  */
 int q8o_quantize_rows(const float *x, int64_t rows, int64_t K,
                       int8_t *q, float *d) {
-    if (K <= 0 || K % Q8_BLOCK != 0 || rows < 0) return -1;
+    if (K < 0 || K % Q8_BLOCK != 0 || rows < 0) return -1;
     const int64_t KB = K / Q8_BLOCK;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
@@ -93,11 +93,12 @@ static int32_t block_dot(const int8_t *a, const int8_t *w) {
 
 /*
  * Per-block integer partials P[i][j][b] (int32, row-major [M][N][K/32]).
+ * K == 0 (no blocks) is accepted throughout: the sums over b are empty.
  * |P| <= 32 * 128 * 128 = 2^19, so int32 is exact.
  */
 int q8o_block_partials(const int8_t *A, const int8_t *W, int32_t *P,
                        int64_t M, int64_t N, int64_t K) {
-    if (M < 0 || N < 0 || K <= 0 || K % Q8_BLOCK != 0) return -1;
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0) return -1;
     const int64_t KB = K / Q8_BLOCK;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t i = 0; i < M; ++i)
@@ -133,7 +134,7 @@ static void qdot_one(const int8_t *A, const float *AS, const int8_t *W,
 int q8o_qdot_f64(const int8_t *A, const float *AS, const int8_t *W,
                  const float *WS, int64_t M, int64_t N, int64_t K,
                  double *out, double *abs_terms) {
-    if (M < 0 || N < 0 || K <= 0 || K % Q8_BLOCK != 0) return -1;
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0) return -1;
 #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j)
@@ -149,7 +150,7 @@ int q8o_qdot_f64_at(const int8_t *A, const float *AS, const int8_t *W,
                     const float *WS, int64_t M, int64_t N, int64_t K,
                     const int64_t *ii, const int64_t *jj, int64_t count,
                     double *out, double *abs_terms) {
-    if (M < 0 || N < 0 || K <= 0 || K % Q8_BLOCK != 0 || count < 0) return -1;
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0 || count < 0) return -1;
     for (int64_t s = 0; s < count; ++s)
         if (ii[s] < 0 || ii[s] >= M || jj[s] < 0 || jj[s] >= N) return -2;
 #pragma omp parallel for schedule(static)
@@ -162,7 +163,7 @@ int q8o_qdot_f64_at(const int8_t *A, const float *AS, const int8_t *W,
 int q8o_block_partials_at(const int8_t *A, const int8_t *W, int64_t M, int64_t N,
                           int64_t K, const int64_t *ii, const int64_t *jj,
                           int64_t count, int32_t *P) {
-    if (M < 0 || N < 0 || K <= 0 || K % Q8_BLOCK != 0 || count < 0) return -1;
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0 || count < 0) return -1;
     for (int64_t s = 0; s < count; ++s)
         if (ii[s] < 0 || ii[s] >= M || jj[s] < 0 || jj[s] >= N) return -2;
     const int64_t KB = K / Q8_BLOCK;

@@ -1,0 +1,116 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function ``include/q8qdot.h`` declares,
+and reject bad arguments with the documented status before anything is
+enqueued.  Only validation paths are called here: each returns before any HIP
+runtime call, so no device is touched.
+"""
+import os
+import re
+
+import pytest
+
+import gemm_q8_qdot_amd as q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8qdot.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    q8.ensure_built()
+    return q8.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared_functions() == sorted(q8.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror(lib):
+    assert q8.q8_version() >= 100
+    for st in (0, -1, -2, -3, -4, -5):
+        assert q8.q8_strerror(st) and q8.q8_strerror(st) != "unknown status"
+    assert q8.q8_strerror(7) == "unknown status"
+
+
+def test_path_dispatch(lib):
+    assert q8.q8_qdot_path(1, 4096, 4096) == 0
+    assert q8.q8_qdot_path(7, 4096, 4096) == 0
+    assert q8.q8_qdot_path(8, 4096, 4096) == 1
+    assert q8.q8_qdot_path(512, 14336, 4096) == 1
+    assert lib.q8_qdot_path(1, 1, 33) == q8.Q8_EINVAL
+    assert lib.q8_qdot_path(-1, 1, 32) == q8.Q8_EINVAL
+
+
+BAD_SHAPES = [(1, 1, 31), (1, 1, -32), (-1, 4, 32), (4, -1, 32), (2, 2, 48)]
+
+
+@pytest.mark.parametrize("M,N,K", BAD_SHAPES)
+def test_bad_shapes_rejected(lib, M, N, K):
+    assert q8.q8_qdot_raw(16, 16, 16, 16, 16, M, N, K) == q8.Q8_EINVAL
+    assert lib.q8_qdot(16, 16, 16, 16, 16, M, N, K) == q8.Q8_EINVAL
+    assert q8.q8_qdot_partials_raw(16, 16, 16, M, N, K) == q8.Q8_EINVAL
+
+
+def test_null_pointers_rejected(lib):
+    ok = 4096
+    for args in [(0, ok, ok, ok, ok), (ok, 0, ok, ok, ok), (ok, ok, 0, ok, ok),
+                 (ok, ok, ok, 0, ok), (ok, ok, ok, ok, 0)]:
+        assert q8.q8_qdot_raw(*args, 1, 64, 64) == q8.Q8_ENULL
+        assert q8.q8_qdot_raw(*args, 64, 64, 64) == q8.Q8_ENULL
+    assert q8.q8_qdot_partials_raw(0, ok, ok, 8, 8, 64) == q8.Q8_ENULL
+    assert q8.q8_qdot_partials_raw(ok, 0, ok, 8, 8, 64) == q8.Q8_ENULL
+    assert q8.q8_qdot_partials_raw(ok, ok, 0, 8, 8, 64) == q8.Q8_ENULL
+    # K == 0 needs only C
+    assert q8.q8_qdot_raw(0, 0, 0, 0, 0, 2, 2, 0) == q8.Q8_ENULL
+    assert q8.q8_quantize_raw(0, ok, ok, 1, 32) == q8.Q8_ENULL
+    assert q8.q8_quantize_raw(ok, 0, ok, 1, 32) == q8.Q8_ENULL
+    assert q8.q8_quantize_raw(ok, ok, 0, 1, 32) == q8.Q8_ENULL
+
+
+def test_misaligned_pointers_rejected(lib):
+    base = 1 << 20
+    # A or W off a 16-byte boundary
+    assert q8.q8_qdot_raw(base + 8, base, base, base, base, 1, 4, 32) == q8.Q8_EALIGN
+    assert q8.q8_qdot_raw(base, base, base + 4, base, base, 64, 4, 32) == q8.Q8_EALIGN
+    # f32 arrays off a 4-byte boundary
+    assert q8.q8_qdot_raw(base, base + 2, base, base, base, 1, 4, 32) == q8.Q8_EALIGN
+    assert q8.q8_qdot_raw(base, base, base, base + 1, base, 1, 4, 32) == q8.Q8_EALIGN
+    assert q8.q8_qdot_raw(base, base, base, base, base + 3, 9, 4, 32) == q8.Q8_EALIGN
+    assert q8.q8_qdot_partials_raw(base, base, base + 2, 9, 4, 32) == q8.Q8_EALIGN
+    assert q8.q8_qdot_partials_raw(base + 1, base, base, 9, 4, 32) == q8.Q8_EALIGN
+    assert q8.q8_quantize_raw(base + 4, base, base, 1, 32) == q8.Q8_EALIGN
+    assert q8.q8_quantize_raw(base, base + 8, base, 1, 32) == q8.Q8_EALIGN
+    assert q8.q8_quantize_raw(base, base, base + 2, 1, 32) == q8.Q8_EALIGN
+
+
+def test_empty_outputs_are_noops(lib):
+    # M == 0 or N == 0: nothing launched, pointers not inspected
+    assert q8.q8_qdot_raw(0, 0, 0, 0, 0, 0, 5, 64) == q8.Q8_OK
+    assert q8.q8_qdot_raw(0, 0, 0, 0, 0, 5, 0, 64) == q8.Q8_OK
+    assert q8.q8_qdot_partials_raw(0, 0, 0, 0, 3, 64) == q8.Q8_OK
+    assert q8.q8_qdot_partials_raw(0, 0, 0, 3, 3, 0) == q8.Q8_OK
+    assert q8.q8_quantize_raw(0, 0, 0, 0, 64) == q8.Q8_OK
+    assert q8.q8_quantize_raw(0, 0, 0, 4, 0) == q8.Q8_OK
+    assert q8.q8_quantize_raw(0, 0, 0, 1, 33) == q8.Q8_EINVAL
+
+
+def test_range_overflow_rejected(lib):
+    big = 2**31 - 32
+    assert q8.q8_qdot_partials_raw(16, 16, 16, big, big, big) == q8.Q8_ERANGE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        q8.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,282 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element.
+
+Bar (stated with the contraction): int32 block partials bit-exact; f32 output
+within ``|C - out64| <= 1e-5 * sum_b |AS*WS*P| + 1e-6`` of the f64 oracle;
+the GPU quantizer bit-exact with the oracle quantizer (both decide each code
+in f32).  Inputs come from the seeded generators in ``synth`` and are
+quantized by the oracle on the host, so no oracle input or expected value
+comes from the GPU.  Every call goes through the C-ABI (``gemm_q8_qdot_amd``
+is a ctypes binding over ``libq8qdot.so``).
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import gemm_q8_qdot_amd as q8
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL, ABS = 1e-5, 1e-6
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU parity tests need a visible gfx950 GPU"
+    q8.ensure_built()
+    q8.load()
+    return torch.device("cuda:0")
+
+
+@functools.lru_cache(maxsize=4)
+def _workload(idx):
+    w = synth.WORKLOADS[idx]
+    a32, w32 = synth.workload_f32(w)
+    A, AS = oracle.quantize_rows(a32)
+    W, WS = oracle.quantize_rows(w32)
+    return A, AS, W, WS
+
+
+def _dev(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def _run(A, AS, W, WS, dev):
+    tA, tAS, tW, tWS = (_dev(x, dev) for x in (A, AS, W, WS))
+    C = q8.q8_qdot(tA, tAS, tW, tWS)
+    P = q8.q8_qdot_partials(tA, tW)
+    torch.cuda.synchronize()
+    return C.cpu().numpy(), P.cpu().numpy()
+
+
+def _assert_close(C, out, mag, what):
+    ok = oracle.within_tolerance(C, out, mag, REL, ABS)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        err = np.abs(C.astype(np.float64) - out)
+        ratio = err / (REL * mag + ABS)
+        k = tuple(np.unravel_index(np.argmax(ratio), ratio.shape))
+        raise AssertionError("%s: %d/%d outside tolerance; worst at %s: C=%r oracle=%r "
+                             "abs_terms=%r (%.3g x bound); first bad %s"
+                             % (what, len(bad), ok.size, k, C[k], out[k], mag[k], ratio[k],
+                                bad[:5].tolist()))
+
+
+def _check_full(A, AS, W, WS, dev, what):
+    _say("[parity] %s M=%d N=%d K=%d" % (what, A.shape[0], W.shape[0], A.shape[1]))
+    C, P = _run(A, AS, W, WS, dev)
+    out, mag = oracle.qdot_f64(A, AS, W, WS)
+    Pref = oracle.block_partials(A, W)
+    assert P.shape == Pref.shape
+    if not np.array_equal(P, Pref):
+        bad = np.argwhere(P != Pref)
+        raise AssertionError("%s: %d partials differ; first %s gpu=%r oracle=%r"
+                             % (what, len(bad), bad[:3].tolist(), P[tuple(bad[0])],
+                                Pref[tuple(bad[0])]))
+    _assert_close(C, out, mag, what)
+    return C, P
+
+
+# ------------------------------------------------------------------ workloads
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+def test_workload_full_output(dev, idx):
+    A, AS, W, WS = _workload(idx)
+    _check_full(A, AS, W, WS, dev, synth.WORKLOADS[idx].name)
+
+
+def test_workload_prompt_size_sampled(dev):
+    # 512 x 14336 x 4096 in the launch configuration the benchmark times;
+    # the oracle checks sampled outputs one by one (whole rows and columns
+    # plus random positions), partials from the full-size debug launch.
+    idx = 4
+    A, AS, W, WS = _workload(idx)
+    M, N = A.shape[0], W.shape[0]
+    _say("[parity] %s sampled" % synth.WORKLOADS[idx].name)
+    tA, tAS, tW, tWS = (_dev(x, dev) for x in (A, AS, W, WS))
+    C = q8.q8_qdot(tA, tAS, tW, tWS)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5151)
+    cols = np.arange(0, N, 7)
+    rows = np.arange(M)
+    ii = np.concatenate([rng.integers(0, M, 3000), np.zeros_like(cols), np.full_like(cols, M - 1),
+                         rows, rows]).astype(np.int64)
+    jj = np.concatenate([rng.integers(0, N, 3000), cols, cols,
+                         np.zeros_like(rows), np.full_like(rows, N - 1)]).astype(np.int64)
+    out, mag = oracle.qdot_f64_at(A, AS, W, WS, ii, jj)
+    Cs = C[torch.from_numpy(ii).to(dev), torch.from_numpy(jj).to(dev)].cpu().numpy()
+    _assert_close(Cs, out, mag, "c4 sampled C")
+    del C
+    P = q8.q8_qdot_partials(tA, tW)
+    torch.cuda.synchronize()
+    Ps = P[torch.from_numpy(ii).to(dev), torch.from_numpy(jj).to(dev)].cpu().numpy()
+    del P
+    torch.cuda.empty_cache()
+    Pref = oracle.block_partials_at(A, W, ii, jj)
+    assert np.array_equal(Ps, Pref)
+
+
+# --------------------------------------------------------------- edge shapes
+
+EDGE = [
+    (1, 1, 32), (1, 37, 1056), (2, 100, 32), (3, 129, 2080), (5, 64, 4096), (7, 300, 1024),
+    (8, 1, 64), (9, 37, 96), (16, 33, 128), (31, 65, 1056), (33, 100, 4096), (63, 129, 320),
+    (64, 4096, 32), (65, 224, 2048), (128, 449, 512), (1, 513, 16416), (3, 8, 32800),
+    (12, 70, 16416), (4, 4099, 14336), (9, 1, 14336),
+]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+def test_edge_shapes(dev, M, N, K):
+    seed = M * 1000003 + N * 101 + K
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 10.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-4, 1.0)
+    _check_full(A, AS, W, WS, dev, "edge")
+
+
+@pytest.mark.parametrize("M", [1, 9])
+def test_extreme_bytes_and_scales(dev, M):
+    N, K = 70, 1024
+    A = np.full((M, K), -128, np.int8)
+    W = synth.random_i8((N, K), 77)
+    W[0] = -128
+    W[1] = 127
+    AS = synth.random_scales((M, K // 32), 78)
+    WS = synth.random_scales((N, K // 32), 79)
+    AS[:, 3] = 1e30
+    WS[:, 3] = 1e-30           # product 1 at block 3
+    AS[:, 5] = 1e-30           # tiny contributions at block 5
+    WS[:, 7] = 0.0             # zero-scale block
+    WS[2] = 0.0                # a whole zero row of scales
+    _check_full(A, AS, W, WS, dev, "extreme")
+
+
+def test_zero_blocks_and_negative_scales(dev):
+    M, N, K = 10, 50, 512
+    A = synth.random_i8((M, K), 88)
+    W = synth.random_i8((N, K), 89)
+    A[:, 64:96] = 0
+    W[:, 128:160] = 0
+    AS = synth.random_scales((M, K // 32), 90) * np.where(np.arange(K // 32) % 3 == 0, -1, 1).astype(np.float32)
+    WS = synth.random_scales((N, K // 32), 91)
+    _check_full(A, AS, W, WS, dev, "zeros/negative scales")
+
+
+# ------------------------------------------------------------ determinism etc.
+
+@pytest.mark.parametrize("idx", [1, 3])
+def test_deterministic(dev, idx):
+    A, AS, W, WS = _workload(idx)
+    tA, tAS, tW, tWS = (_dev(x, dev) for x in (A, AS, W, WS))
+    C1 = q8.q8_qdot(tA, tAS, tW, tWS)
+    C2 = q8.q8_qdot(tA, tAS, tW, tWS)
+    P1 = q8.q8_qdot_partials(tA, tW)
+    P2 = q8.q8_qdot_partials(tA, tW)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+    assert torch.equal(P1, P2)
+
+
+def test_row_chunk_offsets_match_full(dev):
+    # Offset pointers into A/AS (a chunk of rows) give the same rows.
+    A, AS, W, WS = _workload(3)
+    tA, tAS, tW, tWS = (_dev(x, dev) for x in (A, AS, W, WS))
+    full = q8.q8_qdot(tA, tAS, tW, tWS)
+    part = q8.q8_qdot(tA[40:52], tAS[40:52], tW, tWS)
+    one = q8.q8_qdot(tA[17:18], tAS[17:18], tW, tWS)
+    torch.cuda.synchronize()
+    out, mag = oracle.qdot_f64(A[40:52], AS[40:52], W, WS)
+    _assert_close(part.cpu().numpy(), out, mag, "row chunk")
+    out1, mag1 = oracle.qdot_f64(A[17:18], AS[17:18], W, WS)
+    _assert_close(one.cpu().numpy(), out1, mag1, "single row")
+    _assert_close(full[40:52].cpu().numpy(), out, mag, "full rows")
+
+
+def test_output_overwritten_not_accumulated(dev):
+    A = synth.random_i8((9, 64), 5)
+    W = synth.random_i8((20, 64), 6)
+    AS = synth.random_scales((9, 2), 7)
+    WS = synth.random_scales((20, 2), 8)
+    for M in (1, 9):
+        tA, tAS, tW, tWS = (_dev(x, dev) for x in (A[:M], AS[:M], W, WS))
+        C = torch.full((M, 20), 12345.0, device=dev)
+        q8.q8_qdot(tA, tAS, tW, tWS, C)
+        torch.cuda.synchronize()
+        out, mag = oracle.qdot_f64(A[:M], AS[:M], W, WS)
+        _assert_close(C.cpu().numpy(), out, mag, "overwrite M=%d" % M)
+
+
+def test_empty_and_zero_K(dev):
+    e8 = torch.empty((0, 64), dtype=torch.int8, device=dev)
+    C = q8.q8_qdot(e8, torch.empty((0, 2), device=dev), torch.zeros((5, 64), dtype=torch.int8, device=dev),
+                   torch.zeros((5, 2), device=dev))
+    assert C.shape == (0, 5)
+    for M in (1, 9):
+        C = torch.full((M, 6), 7.0, device=dev)
+        q8.q8_qdot(torch.empty((M, 0), dtype=torch.int8, device=dev), torch.empty((M, 0), device=dev),
+                   torch.empty((6, 0), dtype=torch.int8, device=dev), torch.empty((6, 0), device=dev), C)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(C).item() == 0
+
+
+def test_side_stream(dev):
+    A, AS, W, WS = _workload(0)
+    tA, tAS, tW, tWS = (_dev(x, dev) for x in (A, AS, W, WS))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        C = q8.q8_qdot(tA, tAS, tW, tWS)
+    s.synchronize()
+    out, mag = oracle.qdot_f64(A, AS, W, WS)
+    _assert_close(C.cpu().numpy(), out, mag, "side stream")
+
+
+# ------------------------------------------------------------------ quantizer
+
+def _quant_check(x, dev, what):
+    q_ref, d_ref = oracle.quantize_rows(x)
+    Q, D = q8.q8_quantize(_dev(x, dev))
+    torch.cuda.synchronize()
+    Qn, Dn = Q.cpu().numpy(), D.cpu().numpy()
+    assert np.array_equal(Dn.view(np.int32), d_ref.view(np.int32)), what + ": scales differ"
+    if not np.array_equal(Qn, q_ref):
+        bad = np.argwhere(Qn != q_ref)
+        raise AssertionError("%s: %d codes differ, first %s" % (what, len(bad), bad[:3].tolist()))
+
+
+@pytest.mark.parametrize("idx", [0, 2])
+def test_quantizer_workload_rows(dev, idx):
+    w = synth.WORKLOADS[idx]
+    a32, w32 = synth.workload_f32(w, N=512)
+    _quant_check(a32, dev, "activations")
+    _quant_check(w32, dev, "weights")
+
+
+def test_quantizer_golden_and_edges(dev):
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quantize_worked_block.json")))
+    rows = [g["x"], g["zero_block"]["x"], g["nonpower_scale_block"]["x"]]
+    x = np.array(rows, np.float32).reshape(1, -1)
+    _quant_check(x, dev, "golden")
+    Q, D = q8.q8_quantize(_dev(x, dev))
+    torch.cuda.synchronize()
+    assert Q.cpu().numpy()[0, :32].tolist() == g["q"]
+    assert Q.cpu().numpy()[0, 64:96].tolist() == g["nonpower_scale_block"]["q"]
+    y = synth.random_f32((37, 4128), 3)
+    y[0, :32] = 0.0
+    y[1] *= np.float32(1e-30)
+    y[2] *= np.float32(1e30)
+    y[3, 5] = -y[3, :32].__abs__().max() * 2
+    _quant_check(y, dev, "edge rows")
