@@ -25,6 +25,9 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs (the f32 epilogue reads them with plain VALU ops,
+    # no v_accvgpr_read per element).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(REPO, "include"),
 ]
 
@@ -36,29 +39,35 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (need ROCm with gfx950 support)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-D" + d for d in defines] + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libq8qdot.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB_PATH, defines=()) -> str:
+    """Compile every source and link the library; returns its path.
+
+    ``defines`` (``NAME=VALUE`` strings) override the kernels' compile-time
+    launch-shape knobs; ``out`` places such a variant elsewhere.
+    """
+    build_dir = BUILD_DIR if out == LIB_PATH else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB_PATH)
-    return LIB_PATH
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

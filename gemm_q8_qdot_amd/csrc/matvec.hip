@@ -28,10 +28,29 @@
 namespace q8 {
 namespace {
 
+// Launch-shape knobs (compile-time; defaults are the tuned values).
+#ifndef Q8_MV_THREADS
+#define Q8_MV_THREADS 256
+#endif
+#ifndef Q8_MV_MAX_WAVES
+#define Q8_MV_MAX_WAVES (256 * 32)      // short rows: about one row group per wave
+#endif
+#ifndef Q8_MV_MAX_WAVES_LONG
+#define Q8_MV_MAX_WAVES_LONG (256 * 8)  // rows of 8+ KiB: a resident grid that walks rows
+#endif
+#ifndef Q8_MV_LOADS
+#define Q8_MV_LOADS 4
+#endif
+#ifndef Q8_MV_NT
+#define Q8_MV_NT 1
+#endif
+
 constexpr int kStepBytes = kWave * 16;  // one 16-byte load per lane = 1 KiB of a row
-constexpr int kMatvecThreads = 256;     // 4 waves per workgroup
+constexpr int kMatvecThreads = Q8_MV_THREADS;
 constexpr int kMaxSteps = 16;           // activation row resident in VGPRs up to K = 16 KiB
-constexpr int kMatvecMaxWaves = 256 * 16;
+constexpr int kMatvecMaxWaves = Q8_MV_MAX_WAVES;
+constexpr int kMatvecMaxWavesLong = Q8_MV_MAX_WAVES_LONG;
+constexpr int kLoadsInFlight = Q8_MV_LOADS;  // 16-byte weight loads per lane per row group
 
 template <int S, int R, bool PARTIALS>
 __global__ void __launch_bounds__(kMatvecThreads)
@@ -84,7 +103,8 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                 for (int s = 0; s < S; ++s) {
                     const int off = c * chunk + s * kStepBytes + lane * 16;
                     const bool ok = row_ok && off < K;
-                    w[r][s] = ok ? load16_stream(Wj + off) : v4i{0, 0, 0, 0};
+                    w[r][s] = ok ? (Q8_MV_NT ? load16_stream(Wj + off) : load16(Wj + off))
+                                 : v4i{0, 0, 0, 0};
                     if constexpr (!PARTIALS)
                         ws[r][s] = ok ? WS[(int64_t)j * KB + off / kBlock] : 0.0f;
                 }
@@ -119,10 +139,15 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 template <int S, bool PARTIALS>
 hipError_t launch_s(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                     float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    // Rows per wave: about 16 x 16-byte weight loads in flight per lane.
-    constexpr int R = S <= 2 ? 8 : (S <= 4 ? 4 : (S <= 8 ? 2 : 1));
+    // Rows per wave: at least kLoadsInFlight 16-byte weight loads per lane
+    // per row group (more rows only for short rows).  Measured on MI355X:
+    // many light waves beat few heavy ones; long rows (K >= 8 KiB, large
+    // VGPR footprint) prefer a grid that fits the chip at once.
+    constexpr int R0 = kLoadsInFlight / S;
+    constexpr int R = R0 >= 8 ? 8 : (R0 >= 4 ? 4 : (R0 >= 2 ? 2 : 1));
+    constexpr int max_waves = S >= 8 ? kMatvecMaxWavesLong : kMatvecMaxWaves;
     const int groups = (N + R - 1) / R;
-    const int waves = groups < kMatvecMaxWaves ? groups : kMatvecMaxWaves;
+    const int waves = groups < max_waves ? groups : max_waves;
     const int wgs = (waves + kMatvecThreads / kWave - 1) / (kMatvecThreads / kWave);
     dim3 grid(wgs, M);
     matvec_kernel<S, R, PARTIALS><<<grid, kMatvecThreads, 0, stream>>>(A, AS, W, WS, C, P, N, K);

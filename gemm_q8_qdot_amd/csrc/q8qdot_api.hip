@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/q8qdot.h"
+#include "q8qdot.h"
 #include "q8_launch.h"
 
 #define Q8_API extern "C" __attribute__((visibility("default")))
@@ -87,7 +87,7 @@ Q8_API int q8_qdot_partials(const int8_t* A, const int8_t* W, int32_t* P, int M,
 Q8_API int q8_qdot_path(int M, int N, int K) {
     int st = check_shape(M, N, K);
     if (st != Q8_OK) return st;
-    return M <= kMatvecMaxM ? 0 : 1;
+    return M <= kMatvecMaxM ? 0 : q8::qgemm_variant(M, N, K);
 }
 
 Q8_API int q8_quantize(const float* X, int8_t* Q, float* D, int rows, int K, void* stream) {

@@ -5,50 +5,391 @@
 // same sum on integer tensor cores (same table).  One
 // v_mfma_i32_32x32x32_i8 covers exactly one 32-wide Q8_0 block of a 32 x 32
 // output tile, giving the exact int32 block sums P[i, j, b]; the block
-// scales are applied in an f32 epilogue per block.
+// scales are applied per block in an f32 epilogue.  (The K = 64 form would
+// mix two blocks' scales into one sum, so it is not used.)
 //
 // MFMA lane layout relied on (32x32 family, wave64):
-//   operand rows: lane l supplies row (l % 32) of its operand and the 16
-//   bytes k in [16 (l / 32), +16) of the block -- both operands use the same
-//   k split, so the product sums all 32 k of the block whatever order the
-//   hardware uses inside a lane's 16 bytes;
+//   operands: lane l supplies row (l % 32) of its operand and the 16 bytes
+//   k in [16 (l / 32), +16) of the block.  Both operands use the same k
+//   split, so the product sums all 32 k of the block whatever order the
+//   hardware uses inside a lane's 16 bytes.
 //   result: lane l, register r holds D[m][n] with n = l % 32 and
 //   m = 8 (r / 4) + 4 (l / 32) + (r % 4).
 // With the activation tile as the first operand, m is the activation row i
 // and n the weight row j: each lane owns one output column j and 16 rows.
+//
+// Epilogue, 2 f32 VALU ops per (i, j, block): the int32 accumulator input of
+// every MFMA is the constant 0x4B400000, so the result's bits read as the
+// f32 value 12582912 + p (exact for |p| < 2^22; |p| <= 2^19 here).  With
+// ws_hi = WS[j, b] with its two low mantissa bits cleared, ws_hi * 12582912
+// is exact, so
+//     u   = fma(ws_hi, D, -ws_hi * 12582912)   = round(ws_hi * p)
+//     acc = fma(AS[i, b], u, acc)
+// The truncation changes each term by at most 3 ulp (3.6e-7 relative); the
+// int32 partials stay exact (the debug entry subtracts the bias in integer).
+// (ws_hi, -ws_hi * 12582912) pairs are prepared once per workgroup while
+// staging.  Requires |WS| < 2^100 so the bias product stays finite.
+//
+// Two kernels:
+//   staged  -- large M: a 4-wave workgroup owns a 128 x (32 TN) output tile;
+//              A, W and both scale slices are staged through LDS two blocks
+//              at a time (double-buffered), every wave reuses the staged W
+//              tile for its own 32 rows.  One workgroup per CU; tiles are
+//              ordered so the workgroups sharing a W slab sit on one XCD.
+//   simple  -- fallback for shapes with too few large tiles: one wave per
+//              32 x 32 tile, operands read straight from global memory.
 #include "q8_device.h"
 #include "q8_launch.h"
+
+#include <type_traits>
 
 namespace q8 {
 namespace {
 
 constexpr int kTile = 32;
-constexpr int kQgemmWaves = 4;  // waves per workgroup, side by side along N
+constexpr int kBias = 0x4B400000;          // bits of 12582912.0f = 1.5 * 2^23
+constexpr float kBiasF = 12582912.0f;
 
 __device__ __forceinline__ int tile_row(int r, int half) {
     return 8 * (r / 4) + 4 * half + (r % 4);
 }
 
+__device__ __forceinline__ float2 ws_pair(float ws) {
+    const float hi = __int_as_float(__float_as_int(ws) & ~3);
+    return make_float2(hi, hi * -kBiasF);
+}
+
+// ---------------------------------------------------------------- staged
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kMWaves = 4;                      // along M, 32 rows each
+constexpr int kNWaves = 2;                      // along N: tiles 0..3 and 4..TN-1
+constexpr int kStagedWaves = kMWaves * kNWaves; // 8 waves: two per SIMD
+constexpr int kStagedThreads = kStagedWaves * kWave;
+constexpr int kBM = kMWaves * kTile;            // 128 rows of A per workgroup
+constexpr int kSB = 4;                          // Q8_0 blocks per stage
+constexpr int kSeg = kSB * kBlock;              // 128 bytes of a row per stage
+constexpr int kRowsPerLoad = kWave * 16 / kSeg; // one 16-byte-per-lane load: 8 rows
+constexpr int kRing = 3;                        // LDS stages; loads run two stages ahead
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit dwords (gfx9 family)
+constexpr int kNoRead = 0x7FFFFFF0;             // voffset past every range: the load returns 0
+
+// LDS row r holds its eight 16-byte chunks permuted: logical chunk c sits at
+// physical chunk c ^ swz(r).  Sixteen consecutive rows read at the same
+// logical chunk then hit sixteen distinct 16-byte bank groups (with 32 or 64
+// four-byte banks), so the MFMA fragment reads are conflict-free.  swz only
+// depends on r mod 16, so a lane's chunk is the same in every 16-row group.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+constexpr int kWSRows = 256;  // weight-scale rows per block in LDS (BN padded to whole loads)
+
+template <int TN>
+struct StagedStage {
+    static constexpr int BN = TN * kTile;
+    int8_t a[kBM * kSeg];
+    int8_t w[BN * kSeg];
+    float as[kSB][kBM];
+    float ws[kSB][kWSRows];
+};
+
+template <int TN>
+constexpr size_t staged_smem_bytes() {
+    return sizeof(StagedStage<TN>) * kRing;
+}
+
+// Raw buffer descriptor (in SGPRs) for `bytes` bytes at `base`; reads whose
+// offset is past the range return 0.
+__device__ __forceinline__ v4i make_desc(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+    v4i d;
+    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF));  // stride 0
+    d.z = __builtin_amdgcn_readfirstlane(n);
+    d.w = kRsrcWord3;
+    return d;
+}
+
+// Buffer loads straight into LDS (lane l's bytes land at lds + l * size).
+// Issued from inline assembly so that the only waits on them are the
+// explicit vmcnt waits of the stage ring below.  m0 carries the LDS address;
+// nothing else in this kernel keeps a value in m0.
+__device__ __forceinline__ void dma16(v4i desc, uint32_t lds, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void dma4(v4i desc, uint32_t lds, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    // wave-uniform: m0 is a scalar register
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(const lds_char*)p);
+}
+
+template <int TN, bool PARTIALS>
+__global__ void __launch_bounds__(kStagedThreads, 1)
+qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
+                    const int8_t* __restrict__ W, const float* __restrict__ WS,
+                    float* __restrict__ C, int32_t* __restrict__ P, int M, int N, int K,
+                    int tiles_m, int tiles_total) {
+    constexpr int BN = TN * kTile;
+    static_assert(BN <= kWSRows, "weight-scale rows");
+    // Loads of one stage ("jobs"), each one wave-wide instruction:
+    constexpr int kAJobs = kBM / kRowsPerLoad;            // 16: A rows 8q .. 8q+7
+    constexpr int kWJobs = BN / kRowsPerLoad;             // 28: W rows (TN = 7)
+    constexpr int kASJobs = kSB * kBM / kWave;            // 8: activation scales
+    constexpr int kWSJobs = kSB * kWSRows / kWave;        // 16: weight scales
+    constexpr int kJobs = kAJobs + kWJobs + kASJobs + kWSJobs;  // 68
+    constexpr int kMaxPerWave = (kJobs + kStagedWaves - 1) / kStagedWaves;  // 9
+    constexpr int kMinPerWave = kJobs / kStagedWaves;                       // 8
+    constexpr int kBig = kJobs - kMinPerWave * kStagedWaves;               // waves with 9
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    StagedStage<TN>* ring = reinterpret_cast<StagedStage<TN>*>(smem_raw);
+
+    // Tile order: the 8 XCDs take workgroups round-robin; give each XCD a
+    // contiguous run of tiles, M fastest, so the workgroups that share a W
+    // slab run on one XCD and read it through one L2.
+    int tile = blockIdx.x;
+    if (tiles_total % 8 == 0) tile = (blockIdx.x % 8) * (tiles_total / 8) + blockIdx.x / 8;
+    const int tm = tile % tiles_m;
+    const int tn = tile / tiles_m;
+    const int i0 = tm * kBM;
+    const int j0 = tn * BN;
+    const int rows_a = min(M - i0, kBM);
+    const int rows_w = min(N - j0, BN);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    // Wave wv runs on SIMD wv % 4: the two waves of a SIMD share 32 rows of
+    // A and split the TN column tiles 4 + (TN - 4), so every SIMD does TN tiles.
+    const int mw = wv % kMWaves;      // which 32 rows
+    const int nw = wv / kMWaves;      // tiles 0..3 or 4..TN-1
+    const int half = lane / 32;
+    const int col = lane & 31;
+    const int KB = K / kBlock;
+    const int nstages = (KB + kSB - 1) / kSB;
+
+    // Descriptors of this tile's rows: reads past them return 0.
+    const v4i dA = make_desc(A + (int64_t)i0 * K, (int64_t)rows_a * K);
+    const v4i dW = make_desc(W + (int64_t)j0 * K, (int64_t)rows_w * K);
+    const v4i dAS = make_desc(AS + (int64_t)i0 * KB, (int64_t)rows_a * KB * 4);
+    const v4i dWS = make_desc(WS + (int64_t)j0 * KB, (int64_t)rows_w * KB * 4);
+
+    // This wave's jobs: waves 0 .. kBig-1 take 9, the others 8, in order.
+    // A/W job: rows 8 q' .. 8 q' + 7; lane fills physical chunk lane % 8 of
+    // row 8 q' + lane / 8, i.e. reads logical chunk
+    // (lane % 8) ^ swz(8 q' + lane / 8) = (lane % 8) ^ (lane / 8) ^ (q' & 1).
+    // The row goes in the VGPR offset (so the range check sees it), the
+    // stage's byte offset kb0 * 32 in the scalar offset.
+    const int job0 = wv < kBig ? wv * kMaxPerWave : kBig * kMaxPerWave + (wv - kBig) * kMinPerWave;
+    const int njobs = wv < kBig ? kMaxPerWave : kMinPerWave;
+    const int c_even = (lane % 8) ^ (lane / 8);
+    const int voff_row = (lane / 8) * K;          // + 8 q' K per job
+    const int voff_scale = lane * KB * 4;         // + (64 h) KB 4 + s 4 per job
+
+    auto fetch = [&](int st) {
+        StagedStage<TN>& sg = ring[st % kRing];
+        const int kb0 = st * kSB;
+        const int blocks_left = KB - kb0;
+        const bool partial = blocks_left < kSB;
+#pragma unroll
+        for (int u = 0; u < kMaxPerWave; ++u) {
+            if (u < njobs) {
+                const int q = job0 + u;
+                if (q < kAJobs + kWJobs) {
+                    const bool is_a = q < kAJobs;
+                    const int qq = is_a ? q : q - kAJobs;
+                    const int c = c_even ^ (qq & 1);
+                    int vo = voff_row + qq * kRowsPerLoad * K + 16 * c;
+                    if (partial && c / 2 >= blocks_left) vo = kNoRead;  // past K: read 0
+                    if (is_a) dma16(dA, lds_addr(&sg.a[qq * kRowsPerLoad * kSeg]), vo, kb0 * kBlock);
+                    else dma16(dW, lds_addr(&sg.w[qq * kRowsPerLoad * kSeg]), vo, kb0 * kBlock);
+                } else if constexpr (!PARTIALS) {  // the debug entry passes no scales
+                    const bool is_as = q < kAJobs + kWJobs + kASJobs;
+                    const int e = is_as ? q - kAJobs - kWJobs : q - kAJobs - kWJobs - kASJobs;
+                    const int per_blk = is_as ? kBM / kWave : kWSRows / kWave;  // jobs per block
+                    const int sblk = e / per_blk;
+                    const int h = e % per_blk;
+                    const int vo = (partial && sblk >= blocks_left)
+                                       ? kNoRead : voff_scale + h * kWave * KB * 4 + sblk * 4;
+                    if (is_as) dma4(dAS, lds_addr(&sg.as[sblk][h * kWave]), vo, kb0 * 4);
+                    else dma4(dWS, lds_addr(&sg.ws[sblk][h * kWave]), vo, kb0 * 4);
+                }
+            }
+        }
+    };
+
+    // Fragment read offsets: rows 32 t + col of a tile (swz(32 t + col) =
+    // swz(col) for every tile t), logical chunk 2 s + half of block s.
+    int frag_off[kSB];
+#pragma unroll
+    for (int s = 0; s < kSB; ++s) frag_off[s] = col * kSeg + 16 * ((2 * s + half) ^ swz(col));
+
+    v16i bias;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[r] = PARTIALS ? 0 : kBias;
+    constexpr int kT0 = 4;            // tiles of the nw = 0 wave
+    constexpr int kT1 = TN - kT0;     // tiles of the nw = 1 wave
+    static_assert(kT1 >= 1 && kT1 <= kT0, "tile split");
+    float acc[kT0][16];
+#pragma unroll
+    for (int t = 0; t < kT0; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+    // The math of block s (compile-time) of stage st for NT tiles from T0.
+    auto block_math = [&](const StagedStage<TN>& sg, int st, int s, auto nt_const, auto t0_const) {
+        constexpr int NT = decltype(nt_const)::value;
+        constexpr int T0 = decltype(t0_const)::value;
+        const int kb = st * kSB + s;
+        const v4i af = *reinterpret_cast<const v4i*>(sg.a + mw * kTile * kSeg + frag_off[s]);
+        if constexpr (PARTIALS) {
+            if (kb < KB) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (T0 + t) * kTile * kSeg + frag_off[s]);
+                    const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
+                    const int j = j0 + (T0 + t) * kTile + col;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = i0 + mw * kTile + tile_row(r, half);
+                        if (i < M && j < N) P[((int64_t)i * N + j) * KB + kb] = d[r];
+                    }
+                }
+            }
+        } else {
+            // Blocks past K (last stage only) read zero weight scales and
+            // add exactly 0, so there is no per-block branch here.
+            float asv[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&sg.as[s][mw * kTile + 8 * g + 4 * half]);
+                asv[4 * g + 0] = a4.x;
+                asv[4 * g + 1] = a4.y;
+                asv[4 * g + 2] = a4.z;
+                asv[4 * g + 3] = a4.w;
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (T0 + t) * kTile * kSeg + frag_off[s]);
+                const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
+                const float2 wp = ws_pair(sg.ws[s][(T0 + t) * kTile + col]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
+                    acc[t][r] = fmaf(asv[r], u, acc[t][r]);
+                }
+            }
+        }
+    };
+
+    // Prologue: stages 0 and 1 in flight, stage 0 complete.  (The debug
+    // entry skips the scale loads, so its per-wave load counts differ: it
+    // simply waits for everything.)
+    fetch(0);
+    if (nstages > 1 && !PARTIALS) {
+        fetch(1);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0 landed
+    } else {
+        if (nstages > 1) fetch(1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+
+    for (int st = 0; st < nstages; ++st) {
+        const bool ahead = st + 2 < nstages;
+        if (ahead) fetch(st + 2);  // two stages ahead of the math
+        const StagedStage<TN>& sg = ring[st % kRing];
+        if (nw == 0) {
+#pragma unroll
+            for (int s = 0; s < kSB; ++s)
+                block_math(sg, st, s, std::integral_constant<int, kT0>(), std::integral_constant<int, 0>());
+        } else {
+#pragma unroll
+            for (int s = 0; s < kSB; ++s)
+                block_math(sg, st, s, std::integral_constant<int, kT1>(), std::integral_constant<int, kT0>());
+        }
+        // Stage st + 1 has landed once at most this wave's newest loads
+        // (stage st + 2's, 8 or 9 of them) are outstanding; vmcnt(8) also
+        // waits for the oldest of a 9-load wave's stage st + 2 loads.
+        if (ahead && !PARTIALS) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Bare barrier (no fence): the loads of stage st + 2 stay in flight.
+        __builtin_amdgcn_s_barrier();
+    }
+
+    if constexpr (!PARTIALS) {
+        const int T0 = nw == 0 ? 0 : kT0;
+        const int NT = nw == 0 ? kT0 : kT1;
+#pragma unroll
+        for (int t = 0; t < kT0; ++t) {
+            if (t < NT) {
+                const int j = j0 + (T0 + t) * kTile + col;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = i0 + mw * kTile + tile_row(r, half);
+                    if (i < M && j < N) C[(int64_t)i * N + j] = acc[t][r];
+                }
+            }
+        }
+    }
+}
+
+template <int TN, bool PARTIALS>
+hipError_t launch_staged(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    constexpr int BN = TN * kTile;
+    const int tiles_m = (M + kBM - 1) / kBM;
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t total = tiles_m * tiles_n;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    // More than half of the CU's 160 KiB LDS: exactly one workgroup (two
+    // waves per SIMD) per CU.
+    constexpr size_t need = staged_smem_bytes<TN>();
+    constexpr size_t smem = need > 82 * 1024 ? need : 82 * 1024;
+    static_assert(smem <= 160 * 1024, "LDS budget");
+    auto kern = qgemm_staged_kernel<TN, PARTIALS>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    kern<<<dim3((unsigned)total), kStagedThreads, smem, stream>>>(
+        A, AS, W, WS, C, P, M, N, K, tiles_m, (int)total);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- simple
+
+constexpr int kSimpleWaves = 4;  // waves per workgroup, side by side along N
+
 template <bool PARTIALS>
-__global__ void __launch_bounds__(kQgemmWaves * kWave)
+__global__ void __launch_bounds__(kSimpleWaves * kWave)
 qgemm_simple_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
                     float* __restrict__ C, int32_t* __restrict__ P, int M, int N, int K,
                     int n_groups) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
-    const int i0 = (blockIdx.x / n_groups) * kTile;
-    const int j0 = ((blockIdx.x % n_groups) * kQgemmWaves + wv) * kTile;
+    const int64_t i0 = (int64_t)(blockIdx.x / n_groups) * kTile;
+    const int j0 = ((blockIdx.x % n_groups) * kSimpleWaves + wv) * kTile;
     if (j0 >= N) return;  // whole wave
     const int KB = K / kBlock;
     const int half = lane / 32;
-    const int ra = i0 + (lane & 31);
+    const int64_t ra = i0 + (lane & 31);
     const int rw = j0 + (lane & 31);
     const bool a_ok = ra < M;
     const bool w_ok = rw < N;
-    const int8_t* Ap = A + (int64_t)ra * K + 16 * half;
+    const int8_t* Ap = A + ra * K + 16 * half;
     const int8_t* Wp = W + (int64_t)rw * K + 16 * half;
-    const v16i zero = {};
+    v16i bias;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[r] = PARTIALS ? 0 : kBias;
 
     float acc[16];
 #pragma unroll
@@ -57,46 +398,66 @@ qgemm_simple_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     for (int b = 0; b < KB; ++b) {
         const v4i af = a_ok ? load16(Ap + (int64_t)kBlock * b) : v4i{0, 0, 0, 0};
         const v4i wf = w_ok ? load16(Wp + (int64_t)kBlock * b) : v4i{0, 0, 0, 0};
-        const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, zero, 0, 0, 0);
+        const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
         if constexpr (PARTIALS) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int i = i0 + tile_row(r, half);
-                if (i < M && w_ok) P[((int64_t)i * N + rw) * KB + b] = d[r];
+                const int64_t i = i0 + tile_row(r, half);
+                if (i < M && w_ok) P[(i * N + rw) * KB + b] = d[r];
             }
         } else {
-            const float ws = w_ok ? WS[(int64_t)rw * KB + b] : 0.0f;
+            const float2 wp = ws_pair(w_ok ? WS[(int64_t)rw * KB + b] : 0.0f);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int i = i0 + tile_row(r, half);
-                const float as = i < M ? AS[(int64_t)i * KB + b] : 0.0f;
-                acc[r] = fmaf(as * ws, (float)d[r], acc[r]);
+                const int64_t i = i0 + tile_row(r, half);
+                const float as = i < M ? AS[i * KB + b] : 0.0f;
+                const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
+                acc[r] = fmaf(as, u, acc[r]);
             }
         }
     }
     if constexpr (!PARTIALS) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int i = i0 + tile_row(r, half);
-            if (i < M && w_ok) C[(int64_t)i * N + rw] = acc[r];
+            const int64_t i = i0 + tile_row(r, half);
+            if (i < M && w_ok) C[i * N + rw] = acc[r];
         }
     }
 }
 
-}  // namespace
-
-hipError_t launch_qgemm(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    const int n_groups = (N + kTile * kQgemmWaves - 1) / (kTile * kQgemmWaves);
+template <bool PARTIALS>
+hipError_t launch_simple(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    const int n_groups = (N + kTile * kSimpleWaves - 1) / (kTile * kSimpleWaves);
     const int64_t m_tiles = (M + kTile - 1) / kTile;
     const int64_t blocks = m_tiles * n_groups;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)blocks);
-    if (P != nullptr)
-        qgemm_simple_kernel<true><<<grid, kQgemmWaves * kWave, 0, stream>>>(A, AS, W, WS, C, P, M, N, K, n_groups);
-    else
-        qgemm_simple_kernel<false><<<grid, kQgemmWaves * kWave, 0, stream>>>(A, AS, W, WS, C, P, M, N, K, n_groups);
+    qgemm_simple_kernel<PARTIALS><<<dim3((unsigned)blocks), kSimpleWaves * kWave, 0, stream>>>(
+        A, AS, W, WS, C, P, M, N, K, n_groups);
     return hipGetLastError();
+}
+
+constexpr int kStagedTN = 7;  // 128 x 224 tiles: 512 x 14336 is exactly 256 of them
+
+}  // namespace
+
+int qgemm_variant(int M, int N, int K) {
+    // The staged kernel needs enough 128 x 224 tiles to occupy the chip, and
+    // its 32-bit in-tile offsets need 224 K < 2^31.
+    const int64_t BN = kStagedTN * kTile;
+    const int64_t staged_tiles = ((int64_t)M + kBM - 1) / kBM * (((int64_t)N + BN - 1) / BN);
+    const bool staged = M >= kBM && staged_tiles >= 128 && (int64_t)K * BN < ((int64_t)1 << 31);
+    return staged ? 2 : 1;
+}
+
+hipError_t launch_qgemm(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    if (qgemm_variant(M, N, K) == 2) {
+        if (P != nullptr) return launch_staged<kStagedTN, true>(A, AS, W, WS, C, P, M, N, K, stream);
+        return launch_staged<kStagedTN, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    }
+    if (P != nullptr) return launch_simple<true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_simple<false>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 }  // namespace q8

@@ -48,7 +48,10 @@ def test_path_dispatch(lib):
     assert q8.q8_qdot_path(1, 4096, 4096) == 0
     assert q8.q8_qdot_path(7, 4096, 4096) == 0
     assert q8.q8_qdot_path(8, 4096, 4096) == 1
-    assert q8.q8_qdot_path(512, 14336, 4096) == 1
+    assert q8.q8_qdot_path(64, 4096, 4096) == 1
+    assert q8.q8_qdot_path(512, 14336, 4096) == 2
+    assert q8.q8_qdot_path(129, 14336, 96) == 2
+    assert q8.q8_qdot_path(128, 449, 512) == 1
     assert lib.q8_qdot_path(1, 1, 33) == q8.Q8_EINVAL
     assert lib.q8_qdot_path(-1, 1, 32) == q8.Q8_EINVAL
 

@@ -145,7 +145,34 @@ def test_edge_shapes(dev, M, N, K):
     _check_full(A, AS, W, WS, dev, "edge")
 
 
-@pytest.mark.parametrize("M", [1, 9])
+STAGED = [(129, 14336, 96), (136, 14300, 160), (256, 14400, 4128), (512, 14336, 32)]
+
+
+@pytest.mark.parametrize("M,N,K", STAGED)
+def test_staged_gemm_shapes(dev, M, N, K):
+    # Shapes that reach the LDS-staged GEMM, with ragged M, N and a partial
+    # last stage of blocks; f32 output in full, partials at sampled outputs.
+    assert q8.q8_qdot_path(M, N, K) == 2
+    seed = M * 7 + N * 3 + K
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 10.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-4, 1.0)
+    _say("[parity] staged M=%d N=%d K=%d" % (M, N, K))
+    tA, tAS, tW, tWS = (_dev(x, dev) for x in (A, AS, W, WS))
+    C = q8.q8_qdot(tA, tAS, tW, tWS)
+    P = q8.q8_qdot_partials(tA, tW)
+    torch.cuda.synchronize()
+    out, mag = oracle.qdot_f64(A, AS, W, WS)
+    _assert_close(C.cpu().numpy(), out, mag, "staged C")
+    rng = np.random.default_rng(seed)
+    ii = np.concatenate([rng.integers(0, M, 4000), np.full(64, M - 1), np.arange(64) % M]).astype(np.int64)
+    jj = np.concatenate([rng.integers(0, N, 4000), N - 1 - np.arange(64), np.full(64, N - 1)]).astype(np.int64)
+    Ps = P[torch.from_numpy(ii).to(dev), torch.from_numpy(jj).to(dev)].cpu().numpy()
+    assert np.array_equal(Ps, oracle.block_partials_at(A, W, ii, jj))
+
+
+@pytest.mark.parametrize("M", [1, 9, 129])
 def test_extreme_bytes_and_scales(dev, M):
     N, K = 70, 1024
     A = np.full((M, K), -128, np.int8)
