@@ -90,12 +90,12 @@ struct StagedStage {
     int8_t a[kBM * kSeg];
     int8_t w[BN * kSeg];
     float as[kSB][kBM];
-    float ws[kSB][kWSRows];
+    float ws[kSB * kWSRows];  // [block][row] (dword loads) or [row][block] (16-byte loads)
 };
 
 template <int TN>
 constexpr size_t staged_smem_bytes() {
-    return sizeof(StagedStage<TN>) * kRing;
+    return sizeof(StagedStage<TN>) * kRing + 1024;  // + spare area for dummy loads
 }
 
 // Raw buffer descriptor (in SGPRs) for `bytes` bytes at `base`; reads whose
@@ -128,7 +128,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(const lds_char*)p);
 }
 
-template <int TN, bool PARTIALS>
+// WSX4: K/32 is a multiple of the stage's 4 blocks, so every stage is whole
+// and each weight-scale row's 4 block scales come as one 16-byte load
+// (LDS layout [row][block]); otherwise one dword per (block, row) with
+// blocks past K read as 0 (layout [block][row]).
+template <int TN, bool PARTIALS, bool WSX4>
 __global__ void __launch_bounds__(kStagedThreads, 1)
 qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -136,15 +140,19 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     int tiles_m, int tiles_total) {
     constexpr int BN = TN * kTile;
     static_assert(BN <= kWSRows, "weight-scale rows");
-    // Loads of one stage ("jobs"), each one wave-wide instruction:
-    constexpr int kAJobs = kBM / kRowsPerLoad;            // 16: A rows 8q .. 8q+7
-    constexpr int kWJobs = BN / kRowsPerLoad;             // 28: W rows (TN = 7)
-    constexpr int kASJobs = kSB * kBM / kWave;            // 8: activation scales
-    constexpr int kWSJobs = kSB * kWSRows / kWave;        // 16: weight scales
-    constexpr int kJobs = kAJobs + kWJobs + kASJobs + kWSJobs;  // 68
-    constexpr int kMaxPerWave = (kJobs + kStagedWaves - 1) / kStagedWaves;  // 9
-    constexpr int kMinPerWave = kJobs / kStagedWaves;                       // 8
-    constexpr int kBig = kJobs - kMinPerWave * kStagedWaves;               // waves with 9
+    // Loads of one stage ("jobs"), each one wave-wide instruction.  Every
+    // wave has a fixed pattern: A rows 16 wv .. 16 wv + 15 (2 jobs), then its
+    // share of the W rows (4 jobs for waves 0-3, 3 for waves 4-7), then one
+    // activation-scale job (block wv / 2, rows 64 (wv % 2) ..), then weight
+    // scales: with WSX4 one 16-byte job (rows 64 (wv - 4) ..) for waves 4-7,
+    // else two dword jobs per wave (block wv / 2, rows 128 (wv % 2) + 64 k ..).
+    constexpr int kWJobs = BN / kRowsPerLoad;             // 28 for TN = 7
+    static_assert(kBM / kRowsPerLoad == 2 * kStagedWaves, "two A jobs per wave");
+    static_assert(kWJobs == 4 * 4 + 4 * 3, "W jobs: 4 per wave for waves 0-3, 3 for waves 4-7");
+    static_assert(kSB * kBM / kWave == kStagedWaves, "one activation-scale job per wave");
+    static_assert(kWSRows * 16 / 1024 == 4 && kSB * kWSRows / kWave == 2 * kStagedWaves, "weight-scale jobs");
+    // loads per wave per stage (all waves): 2 A + 4 W + activation scales + weight scales
+    constexpr int kLoadsPerWave = PARTIALS ? 6 : (WSX4 ? 8 : 9);
     extern __shared__ __align__(16) unsigned char smem_raw[];
     StagedStage<TN>* ring = reinterpret_cast<StagedStage<TN>*>(smem_raw);
 
@@ -178,48 +186,92 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const v4i dAS = make_desc(AS + (int64_t)i0 * KB, (int64_t)rows_a * KB * 4);
     const v4i dWS = make_desc(WS + (int64_t)j0 * KB, (int64_t)rows_w * KB * 4);
 
-    // This wave's jobs: waves 0 .. kBig-1 take 9, the others 8, in order.
-    // A/W job: rows 8 q' .. 8 q' + 7; lane fills physical chunk lane % 8 of
+    // A/W job of rows 8 q' .. 8 q' + 7: lane fills physical chunk lane % 8 of
     // row 8 q' + lane / 8, i.e. reads logical chunk
     // (lane % 8) ^ swz(8 q' + lane / 8) = (lane % 8) ^ (lane / 8) ^ (q' & 1).
     // The row goes in the VGPR offset (so the range check sees it), the
-    // stage's byte offset kb0 * 32 in the scalar offset.
-    const int job0 = wv < kBig ? wv * kMaxPerWave : kBig * kMaxPerWave + (wv - kBig) * kMinPerWave;
-    const int njobs = wv < kBig ? kMaxPerWave : kMinPerWave;
+    // stage's byte offset in the scalar offset.
     const int c_even = (lane % 8) ^ (lane / 8);
-    const int voff_row = (lane / 8) * K;          // + 8 q' K per job
-    const int voff_scale = lane * KB * 4;         // + (64 h) KB 4 + s 4 per job
+    const int voff_even = (lane / 8) * K + 16 * c_even;
+    const int voff_odd = (lane / 8) * K + 16 * (c_even ^ 1);
+    const int voff_scale = lane * KB * 4;
+    const int w_first = wv < 4 ? 4 * wv : 16 + 3 * (wv - 4);  // first W job of this wave
+    const int w_count = wv < 4 ? 4 : 3;
 
-    auto fetch = [&](int st) {
+    // The issue code below has no branches: a load that must not happen
+    // (past the last stage, a wave's missing fourth W job or its missing
+    // weight-scale job) still issues, with voffset kNoRead (reads nothing,
+    // writes zeros) into the spare LDS area past the ring.  Every wave thus
+    // issues the same number of loads per stage, and the math stays one
+    // straight run of code the register allocator handles well.
+    uint8_t* spare = smem_raw + sizeof(StagedStage<TN>) * kRing;
+
+    // One A/W job (rows 8 qq ..) of stage st; `real` false: a dummy load.
+    auto job_rows = [&](int st, bool is_a, int qq, bool real) {
         StagedStage<TN>& sg = ring[st % kRing];
         const int kb0 = st * kSB;
-        const int blocks_left = KB - kb0;
-        const bool partial = blocks_left < kSB;
+        int vo = ((qq & 1) ? voff_odd : voff_even) + qq * kRowsPerLoad * K;
+        if constexpr (!WSX4) {  // the last stage may be partial: chunks past K read 0
+            const int blocks_left = KB - kb0;
+            const int c = c_even ^ (qq & 1);
+            vo = (blocks_left < kSB && c / 2 >= blocks_left) ? kNoRead : vo;
+        }
+        vo = real ? vo : kNoRead;
+        const void* dst = real ? (is_a ? (const void*)&sg.a[qq * kRowsPerLoad * kSeg]
+                                       : (const void*)&sg.w[qq * kRowsPerLoad * kSeg])
+                               : (const void*)spare;
+        dma16(is_a ? dA : dW, lds_addr(dst), vo, kb0 * kBlock);
+    };
+    // The scale jobs of stage st (none in the debug entry, which has no scales).
+    auto job_scales = [&](int st, bool real) {
+        if constexpr (!PARTIALS) {
+            StagedStage<TN>& sg = ring[st % kRing];
+            const int kb0 = st * kSB;
+            const int blocks_left = KB - kb0;
+            {   // activation scales: block wv / 2, rows 64 (wv % 2) + lane
+                const int sblk = wv / 2, h = wv % 2;
+                const bool ok = real && sblk < blocks_left;
+                const int vo = ok ? voff_scale + h * kWave * KB * 4 + sblk * 4 : kNoRead;
+                dma4(dAS, lds_addr(real ? (const void*)&sg.as[sblk][h * kWave] : (const void*)spare), vo, kb0 * 4);
+            }
+            if constexpr (WSX4) {
+                // waves 4-7: rows 64 e + lane, blocks kb0 .. kb0 + 3 (rows past
+                // the tile read 0); waves 0-3: a dummy load
+                const int e = wv - 4;
+                const bool ok = real && wv >= 4;
+                const int vo = ok ? voff_scale + e * kWave * KB * 4 : kNoRead;
+                dma16(dWS, lds_addr(ok ? (const void*)&sg.ws[e * kWave * kSB] : (const void*)spare), vo, kb0 * 4);
+            } else {
 #pragma unroll
-        for (int u = 0; u < kMaxPerWave; ++u) {
-            if (u < njobs) {
-                const int q = job0 + u;
-                if (q < kAJobs + kWJobs) {
-                    const bool is_a = q < kAJobs;
-                    const int qq = is_a ? q : q - kAJobs;
-                    const int c = c_even ^ (qq & 1);
-                    int vo = voff_row + qq * kRowsPerLoad * K + 16 * c;
-                    if (partial && c / 2 >= blocks_left) vo = kNoRead;  // past K: read 0
-                    if (is_a) dma16(dA, lds_addr(&sg.a[qq * kRowsPerLoad * kSeg]), vo, kb0 * kBlock);
-                    else dma16(dW, lds_addr(&sg.w[qq * kRowsPerLoad * kSeg]), vo, kb0 * kBlock);
-                } else if constexpr (!PARTIALS) {  // the debug entry passes no scales
-                    const bool is_as = q < kAJobs + kWJobs + kASJobs;
-                    const int e = is_as ? q - kAJobs - kWJobs : q - kAJobs - kWJobs - kASJobs;
-                    const int per_blk = is_as ? kBM / kWave : kWSRows / kWave;  // jobs per block
-                    const int sblk = e / per_blk;
-                    const int h = e % per_blk;
-                    const int vo = (partial && sblk >= blocks_left)
-                                       ? kNoRead : voff_scale + h * kWave * KB * 4 + sblk * 4;
-                    if (is_as) dma4(dAS, lds_addr(&sg.as[sblk][h * kWave]), vo, kb0 * 4);
-                    else dma4(dWS, lds_addr(&sg.ws[sblk][h * kWave]), vo, kb0 * 4);
+                for (int k = 0; k < 2; ++k) {  // block wv / 2, rows 128 (wv % 2) + 64 k + lane
+                    const int sblk = wv / 2, h = 2 * (wv % 2) + k;
+                    const bool ok = real && sblk < blocks_left;
+                    const int vo = ok ? voff_scale + h * kWave * KB * 4 + sblk * 4 : kNoRead;
+                    dma4(dWS, lds_addr(real ? (const void*)&sg.ws[sblk * kWSRows + h * kWave] : (const void*)spare),
+                         vo, kb0 * 4);
                 }
             }
         }
+    };
+    // Slice p (0..3) of the loads of stage st: slices go between the four
+    // blocks of math so the load queue never backs up into the math.
+    auto fetch_slice = [&](int st, int p, bool real) {
+        if (p == 0) {
+            job_rows(st, true, 2 * wv, real);
+            job_rows(st, true, 2 * wv + 1, real);
+        } else if (p == 1) {
+            job_rows(st, false, w_first, real);
+            job_rows(st, false, w_first + 1, real);
+        } else if (p == 2) {
+            job_rows(st, false, w_first + 2, real);
+            job_rows(st, false, w_first + 3, real && w_count == 4);
+        } else {
+            job_scales(st, real);
+        }
+    };
+    auto fetch = [&](int st) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) fetch_slice(st, p, true);
     };
 
     // Fragment read offsets: rows 32 t + col of a tile (swz(32 t + col) =
@@ -231,19 +283,24 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     v16i bias;
 #pragma unroll
     for (int r = 0; r < 16; ++r) bias[r] = PARTIALS ? 0 : kBias;
-    constexpr int kT0 = 4;            // tiles of the nw = 0 wave
-    constexpr int kT1 = TN - kT0;     // tiles of the nw = 1 wave
-    static_assert(kT1 >= 1 && kT1 <= kT0, "tile split");
+    // Opaque to the optimizer: the tile stays in 16 VGPRs instead of being
+    // rebuilt from a scalar before every block.
+    asm volatile("" : "+v"(bias));
+    constexpr int kT0 = 4;            // accumulator slots per wave
+    static_assert(TN == 7, "the two waves of a SIMD split 7 tiles as 3 + 3 + (1 split by blocks)");
     float acc[kT0][16];
 #pragma unroll
     for (int t = 0; t < kT0; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-    // The math of block s (compile-time) of stage st for NT tiles from T0.
-    auto block_math = [&](const StagedStage<TN>& sg, int st, int s, auto nt_const, auto t0_const) {
-        constexpr int NT = decltype(nt_const)::value;
+    // The math of block s (compile-time) of stage st for NT tiles from T0;
+    // wsp[t][s] holds the (ws_hi, bias product) pair of tile t, block s.
+    auto block_math = [&](const StagedStage<TN>& sg, int st, int s, auto nt_const, auto t0_const,
+                          auto slot0_const, const float2 (&wsp)[kT0][kSB]) {
+        constexpr int NT = decltype(nt_const)::value;    // tiles T0 .. T0 + NT - 1
         constexpr int T0 = decltype(t0_const)::value;
+        constexpr int SL = decltype(slot0_const)::value; // accumulator slot of tile T0
         const int kb = st * kSB + s;
         const v4i af = *reinterpret_cast<const v4i*>(sg.a + mw * kTile * kSeg + frag_off[s]);
         if constexpr (PARTIALS) {
@@ -276,71 +333,122 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             for (int t = 0; t < NT; ++t) {
                 const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (T0 + t) * kTile * kSeg + frag_off[s]);
                 const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
-                const float2 wp = ws_pair(sg.ws[s][(T0 + t) * kTile + col]);
+                const float2 wp = wsp[SL + t][s];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
-                    acc[t][r] = fmaf(asv[r], u, acc[t][r]);
+                    acc[SL + t][r] = fmaf(asv[r], u, acc[SL + t][r]);
                 }
             }
         }
     };
+    // The weight-scale pairs of this wave's NT tiles for the whole stage
+    // (one 16-byte read per tile in the [row][block] layout: conflict-free).
+    auto load_wsp = [&](const StagedStage<TN>& sg, auto nt_const, auto t0_const, float2 (&wsp)[kT0][kSB]) {
+        constexpr int NT = decltype(nt_const)::value;    // slots 0 .. NT-1 = tiles T0 ..
+        constexpr int T0 = decltype(t0_const)::value;
+        if constexpr (!PARTIALS) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int wrow = (T0 + t) * kTile + col;
+                float w4[kSB];
+                if constexpr (WSX4) {
+                    const float4 v = *reinterpret_cast<const float4*>(&sg.ws[wrow * kSB]);
+                    w4[0] = v.x; w4[1] = v.y; w4[2] = v.z; w4[3] = v.w;
+                } else {
+#pragma unroll
+                    for (int s = 0; s < kSB; ++s) w4[s] = sg.ws[s * kWSRows + wrow];
+                }
+#pragma unroll
+                for (int s = 0; s < kSB; ++s) wsp[t][s] = ws_pair(w4[s]);
+            }
+        }
+    };
 
-    // Prologue: stages 0 and 1 in flight, stage 0 complete.  (The debug
-    // entry skips the scale loads, so its per-wave load counts differ: it
-    // simply waits for everything.)
+    // Stage st + 1 has landed once at most this wave's kLoadsPerWave newest
+    // loads (those of stage st + 2) are outstanding (loads complete in order).
+    auto wait_vmcnt_stage = [&]() {
+        if constexpr (kLoadsPerWave == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        else if constexpr (kLoadsPerWave == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    };
+
+    // Prologue: stages 0 and 1 in flight, stage 0 complete.
     fetch(0);
-    if (nstages > 1 && !PARTIALS) {
-        fetch(1);
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0 landed
-    } else {
-        if (nstages > 1) fetch(1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) fetch_slice(1, p, nstages > 1);
+    wait_vmcnt_stage();
     __builtin_amdgcn_s_barrier();
 
     for (int st = 0; st < nstages; ++st) {
         const bool ahead = st + 2 < nstages;
-        if (ahead) fetch(st + 2);  // two stages ahead of the math
         const StagedStage<TN>& sg = ring[st % kRing];
+        // Loads of stage st + 2 (two ahead), interleaved with this stage's math.
+        // Tiles: wave nw = 0 owns 0, 1, 2 and blocks 0, 1 of tile 3 (slot 3);
+        // nw = 1 owns 4, 5, 6 (slots 1-3) and blocks 2, 3 of tile 3 (slot 0):
+        // 14 tile-blocks each per stage.
+        float2 wsp[kT0][kSB];
         if (nw == 0) {
+            load_wsp(sg, std::integral_constant<int, 4>(), std::integral_constant<int, 0>(), wsp);
 #pragma unroll
-            for (int s = 0; s < kSB; ++s)
-                block_math(sg, st, s, std::integral_constant<int, kT0>(), std::integral_constant<int, 0>());
+            for (int s = 0; s < kSB; ++s) {
+                fetch_slice(st + 2, s, ahead);
+                if (s < 2)
+                    block_math(sg, st, s, std::integral_constant<int, 4>(), std::integral_constant<int, 0>(),
+                               std::integral_constant<int, 0>(), wsp);
+                else
+                    block_math(sg, st, s, std::integral_constant<int, 3>(), std::integral_constant<int, 0>(),
+                               std::integral_constant<int, 0>(), wsp);
+            }
         } else {
+            load_wsp(sg, std::integral_constant<int, 4>(), std::integral_constant<int, 3>(), wsp);
 #pragma unroll
-            for (int s = 0; s < kSB; ++s)
-                block_math(sg, st, s, std::integral_constant<int, kT1>(), std::integral_constant<int, kT0>());
+            for (int s = 0; s < kSB; ++s) {
+                fetch_slice(st + 2, s, ahead);
+                if (s < 2)
+                    block_math(sg, st, s, std::integral_constant<int, 3>(), std::integral_constant<int, 4>(),
+                               std::integral_constant<int, 1>(), wsp);
+                else
+                    block_math(sg, st, s, std::integral_constant<int, 4>(), std::integral_constant<int, 3>(),
+                               std::integral_constant<int, 0>(), wsp);
+            }
         }
-        // Stage st + 1 has landed once at most this wave's newest loads
-        // (stage st + 2's, 8 or 9 of them) are outstanding; vmcnt(8) also
-        // waits for the oldest of a 9-load wave's stage st + 2 loads.
-        if (ahead && !PARTIALS) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vmcnt_stage();
         // Bare barrier (no fence): the loads of stage st + 2 stay in flight.
         __builtin_amdgcn_s_barrier();
     }
 
     if constexpr (!PARTIALS) {
-        const int T0 = nw == 0 ? 0 : kT0;
-        const int NT = nw == 0 ? kT0 : kT1;
+        // Tile 3 = (blocks 0, 1 of every stage, wave nw = 0) + (blocks 2, 3,
+        // wave nw = 1), added in this fixed order (deterministic).
+        float* red = reinterpret_cast<float*>(smem_raw) + (size_t)mw * 16 * kWave;
+        if (nw == 1) {
 #pragma unroll
-        for (int t = 0; t < kT0; ++t) {
-            if (t < NT) {
-                const int j = j0 + (T0 + t) * kTile + col;
+            for (int r = 0; r < 16; ++r) red[r * kWave + lane] = acc[0][r];
+        }
+        __syncthreads();
+        if (nw == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[3][r] += red[r * kWave + lane];
+        }
+        const int tb = nw == 0 ? 0 : 3;  // tile of slot 0
+#pragma unroll
+        for (int sl = 0; sl < kT0; ++sl) {
+            if (nw == 0 || sl > 0) {
+                const int j = j0 + (tb + sl) * kTile + col;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = i0 + mw * kTile + tile_row(r, half);
-                    if (i < M && j < N) C[(int64_t)i * N + j] = acc[t][r];
+                    if (i < M && j < N) C[(int64_t)i * N + j] = acc[sl][r];
                 }
             }
         }
     }
 }
 
-template <int TN, bool PARTIALS>
-hipError_t launch_staged(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+template <int TN, bool PARTIALS, bool WSX4>
+hipError_t launch_staged_v(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                           float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     constexpr int BN = TN * kTile;
     const int tiles_m = (M + kBM - 1) / kBM;
     const int64_t tiles_n = (N + BN - 1) / BN;
@@ -351,7 +459,7 @@ hipError_t launch_staged(const int8_t* A, const float* AS, const int8_t* W, cons
     constexpr size_t need = staged_smem_bytes<TN>();
     constexpr size_t smem = need > 82 * 1024 ? need : 82 * 1024;
     static_assert(smem <= 160 * 1024, "LDS budget");
-    auto kern = qgemm_staged_kernel<TN, PARTIALS>;
+    auto kern = qgemm_staged_kernel<TN, PARTIALS, WSX4>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -362,6 +470,15 @@ hipError_t launch_staged(const int8_t* A, const float* AS, const int8_t* W, cons
     kern<<<dim3((unsigned)total), kStagedThreads, smem, stream>>>(
         A, AS, W, WS, C, P, M, N, K, tiles_m, (int)total);
     return hipGetLastError();
+}
+
+template <int TN, bool PARTIALS>
+hipError_t launch_staged(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    // 16-byte weight-scale loads need whole stages and a 16-byte aligned WS.
+    if ((K / kBlock) % kSB == 0 && (reinterpret_cast<uintptr_t>(WS) & 15) == 0)
+        return launch_staged_v<TN, PARTIALS, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_staged_v<TN, PARTIALS, false>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 // ---------------------------------------------------------------- simple
