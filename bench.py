@@ -51,8 +51,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS for the headline")
     ap.add_argument("--second", type=int, default=4, help="second measured workload (-1: none)")
+    ap.add_argument("--others", default="0,2,3", help="other workloads timed briefly ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
     ap.add_argument("--no-rotate", action="store_true", help="reuse one copy (cache-warm number)")
+    ap.add_argument("--profile", action="store_true",
+                    help="only launch the headline kernel (for rocprofv3 counter passes)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB 10 times and exit (counter calibration)")
     return ap.parse_args()
 
 
@@ -113,6 +118,47 @@ def time_launches(torch, q8, ops: Operands, steps: int, warmup: int):
     return ms / steps, wall
 
 
+def kernel_source_sha(path: str) -> str:
+    """SHA-256 of the sources a kernel is built from (ties counters to code)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_q8_qdot_amd", "csrc")
+    for name in (path, "q8_device.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, source: str):
+    """HBM bytes per launch from the committed counter record, or None.
+
+    profiles/traffic.json holds FETCH_SIZE and WRITE_SIZE per dispatch for a
+    workload, each scaled by the factor the same counter gives on a plain
+    copy of known size, with the hash of the kernel source they were taken
+    on; a changed kernel makes the record stale (None).
+    """
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha(source):
+        return None
+    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+
+
+def copy_calibration(torch, mib: int):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 10}), flush=True)
+
+
 def cpu_baseline(ops_w: synth.Workload, budget_s: float):
     """The oracle as it stands, on this host, on a bounded sample of the workload."""
     import oracle
@@ -127,8 +173,6 @@ def cpu_baseline(ops_w: synth.Workload, budget_s: float):
         oracle.qdot_f64(A, AS, W, WS)
         times.append(time.perf_counter() - t0)
         if len(times) >= 3 and time.perf_counter() - t_all >= budget_s:
-            break
-        if len(times) >= 1000:
             break
     per = statistics.median(times)
     wbytes = W.nbytes + WS.nbytes
@@ -168,6 +212,15 @@ def main():
         sys.exit(1)
     q8.ensure_built()
     q8.load()
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
+    if args.profile:
+        args.second = -1
+        args.others = ""
+        args.cpu_seconds = 0
+        args.steps = min(args.steps, 50)
+        args.warmup = min(args.warmup, 5)
 
     head_w = synth.WORKLOADS[args.workload]
     log("[bench] preparing %s" % head_w.name)
@@ -178,6 +231,8 @@ def main():
     achieved = head.algo_bytes / (ms * 1e-3) / 1e9
     weight_gbs = head.weight_bytes / (ms * 1e-3) / 1e9
     path = q8.q8_qdot_path(head_w.M, head_w.N, head_w.K)
+    source = "matvec.hip" if path == 0 else "qgemm.hip"
+    traffic = measured_traffic(head_w.name, source)
     dtype = "i8xi8->i32, f32 scales"
     result = {
         "metric": "Q8_0 matvec weight GB/s (M=1)",
@@ -196,7 +251,7 @@ def main():
                    "kernel": "matvec" if path == 0 else "qgemm",
                    "rotated_copies": head.R, "arith": dtype},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": head.algo_bytes,
                      "kernel_us": round(ms * 1e3, 3)},
     }
@@ -224,10 +279,30 @@ def main():
             "valu_floor_frac": round(valu_floor_us / (ms2 * 1e3), 4),
             "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
             "rotated_copies": sec.R,
+            "traffic": measured_traffic(sw.name, "qgemm.hip"),
         }
         log("[bench] second %s: %.3f us/launch, %.1f int8 TOPS (%.1f%% of peak), VALU floor %.1f us"
             % (sw.name, ms2 * 1e3, tops, 100 * tops / INT8_PEAK_TOPS, valu_floor_us))
         del sec
+        torch.cuda.empty_cache()
+
+    others = [int(x) for x in args.others.split(",") if x.strip() != ""]
+    if others:
+        result["others"] = []
+    for idx in others:
+        ow = synth.WORKLOADS[idx]
+        ops = Operands(torch, q8, ow, rotate=not args.no_rotate)
+        ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
+        rec = {"workload": ow.name, "M": ow.M, "N": ow.N, "K": ow.K,
+               "kernel": ["matvec", "qgemm_simple", "qgemm_staged"][q8.q8_qdot_path(ow.M, ow.N, ow.K)],
+               "us_per_launch": round(ms3 * 1e3, 3),
+               "hbm_gbs": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9, 1),
+               "hbm_frac": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "int8_tops": round(ops.int8_ops / (ms3 * 1e-3) / 1e12, 2)}
+        result["others"].append(rec)
+        log("[bench] %s: %.3f us/launch, %.1f GB/s (%.1f%% HBM), %.1f int8 TOPS"
+            % (ow.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"], rec["int8_tops"]))
+        del ops
         torch.cuda.empty_cache()
 
     if args.cpu_seconds > 0:
