@@ -31,11 +31,13 @@
 // staging.  Requires |WS| < 2^100 so the bias product stays finite.
 //
 // Two kernels:
-//   staged  -- large M: a 4-wave workgroup owns a 128 x (32 TN) output tile;
-//              A, W and both scale slices are staged through LDS two blocks
-//              at a time (double-buffered), every wave reuses the staged W
-//              tile for its own 32 rows.  One workgroup per CU; tiles are
-//              ordered so the workgroups sharing a W slab sit on one XCD.
+//   staged  -- large M: an 8-wave workgroup (4 along M x 2 along N) owns a
+//              128 x (32 TN) output tile; A, W and both scale slices are
+//              staged through LDS four blocks (128 k) at a time in a 3-stage
+//              ring filled by direct global->LDS loads, each issued between
+//              the MFMA/epilogue work of an earlier stage.  One workgroup per
+//              CU; tiles are ordered so the workgroups sharing a W slab sit
+//              on one XCD.
 //   simple  -- fallback for shapes with too few large tiles: one wave per
 //              32 x 32 tile, operands read straight from global memory.
 #include "q8_device.h"
