@@ -38,6 +38,8 @@ INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POP/s)
 VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
 EPILOGUE_VALU_OPS = 2            # f32 VALU ops per (i, j, block) in the MFMA epilogue
 CACHE_DEFEAT_BYTES = 1 << 30     # rotate >= 1 GiB of distinct operand copies
+KERNEL_NAMES = ("matvec", "qgemm_ksplit", "qgemm_staged")          # by q8_qdot_path
+KERNEL_SOURCES = ("matvec.hip", "qgemm_ksplit.hip", "qgemm.hip")   # their csrc files
 
 
 def log(msg):
@@ -231,7 +233,7 @@ def main():
     achieved = head.algo_bytes / (ms * 1e-3) / 1e9
     weight_gbs = head.weight_bytes / (ms * 1e-3) / 1e9
     path = q8.q8_qdot_path(head_w.M, head_w.N, head_w.K)
-    source = "matvec.hip" if path == 0 else "qgemm.hip"
+    source = KERNEL_SOURCES[path]
     traffic = measured_traffic(head_w.name, source)
     dtype = "i8xi8->i32, f32 scales"
     result = {
@@ -248,7 +250,7 @@ def main():
         "dtype": "i8",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations, Q8_0-quantized on GPU)",
         "config": {"workload": head_w.name, "M": head_w.M, "N": head_w.N, "K": head_w.K,
-                   "kernel": "matvec" if path == 0 else "qgemm",
+                   "kernel": KERNEL_NAMES[path],
                    "rotated_copies": head.R, "arith": dtype},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -279,7 +281,7 @@ def main():
             "valu_floor_frac": round(valu_floor_us / (ms2 * 1e3), 4),
             "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
             "rotated_copies": sec.R,
-            "traffic": measured_traffic(sw.name, "qgemm.hip"),
+            "traffic": measured_traffic(sw.name, KERNEL_SOURCES[q8.q8_qdot_path(sw.M, sw.N, sw.K)]),
         }
         log("[bench] second %s: %.3f us/launch, %.1f int8 TOPS (%.1f%% of peak), VALU floor %.1f us"
             % (sw.name, ms2 * 1e3, tops, 100 * tops / INT8_PEAK_TOPS, valu_floor_us))
@@ -294,7 +296,7 @@ def main():
         ops = Operands(torch, q8, ow, rotate=not args.no_rotate)
         ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
         rec = {"workload": ow.name, "M": ow.M, "N": ow.N, "K": ow.K,
-               "kernel": ["matvec", "qgemm_simple", "qgemm_staged"][q8.q8_qdot_path(ow.M, ow.N, ow.K)],
+               "kernel": KERNEL_NAMES[q8.q8_qdot_path(ow.M, ow.N, ow.K)],
                "us_per_launch": round(ms3 * 1e3, 3),
                "hbm_gbs": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9, 1),
                "hbm_frac": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

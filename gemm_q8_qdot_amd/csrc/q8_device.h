@@ -67,4 +67,33 @@ __device__ __forceinline__ v4i load16_stream(const int8_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
 
+// ---- v_mfma_i32_32x32x32_i8 (one 32-wide Q8_0 block of a 32 x 32 tile) ----
+// Lane l supplies row l % 32 of each operand and the 16 bytes
+// k in [16 (l / 32), +16) of the block; register r of the result holds
+// D[m][n] with n = l % 32 and m = tile_row(r, l / 32).
+constexpr int kTile = 32;
+constexpr int kBias = 0x4B400000;  // bits of 12582912.0f = 1.5 * 2^23
+constexpr float kBiasF = 12582912.0f;
+
+__device__ __forceinline__ int tile_row(int r, int half) {
+    return 8 * (r / 4) + 4 * half + (r % 4);
+}
+
+// (ws_hi, -12582912 ws_hi): ws with its two low mantissa bits cleared, so
+// that the product with the bias is exact.  With D = the MFMA result seeded
+// with kBias (bits of the f32 12582912 + p), fma(ws_hi, D, -12582912 ws_hi)
+// is ws_hi * p rounded once.
+__device__ __forceinline__ float2 ws_pair(float ws) {
+    const float hi = __int_as_float(__float_as_int(ws) & ~3);
+    return make_float2(hi, hi * -kBiasF);
+}
+
+// LDS tiles of 128-byte row segments (four Q8_0 blocks = eight 16-byte
+// chunks per row): row r holds its chunks permuted, logical chunk c at
+// physical chunk c ^ swz(r).  Sixteen consecutive rows read at the same
+// logical chunk then hit sixteen distinct 16-byte bank groups (with 32 or 64
+// four-byte banks), so the MFMA fragment reads are conflict-free.  swz only
+// depends on r mod 16, so a lane's chunk is the same in every 16-row group.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 }  // namespace q8

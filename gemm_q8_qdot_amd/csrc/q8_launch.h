@@ -15,11 +15,14 @@ hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, cons
                          float* C, int32_t* P, int M, int N, int K, hipStream_t stream);
 
 // M >= 8: int8-MFMA block GEMM.  Same P convention.
-// qgemm_variant: 1 = per-wave 32 x 32 tiles read from global memory,
-// 2 = LDS-staged 128 x 224 workgroup tiles (large M and N).
+// qgemm_variant: 1 = one workgroup per 32 x 32 tile with the contraction
+// split across its waves (few tiles), 2 = LDS-staged 128 x 224 workgroup
+// tiles (large M and N).
 int qgemm_variant(int M, int N, int K);
 hipError_t launch_qgemm(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream);
+hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                               float* C, int32_t* P, int M, int N, int K, hipStream_t stream);
 
 // Q8_0 quantization of f32 rows.
 hipError_t launch_quantize(const float* X, int8_t* Q, float* D, int rows, int K,

@@ -38,8 +38,9 @@
 //              the MFMA/epilogue work of an earlier stage.  One workgroup per
 //              CU; tiles are ordered so the workgroups sharing a W slab sit
 //              on one XCD.
-//   simple  -- fallback for shapes with too few large tiles: one wave per
-//              32 x 32 tile, operands read straight from global memory.
+//   (shapes with too few large tiles go to qgemm_ksplit.hip: one
+//              workgroup per 32 x 32 tile, the contraction split across its
+//              waves.)
 #include "q8_device.h"
 #include "q8_launch.h"
 
@@ -48,18 +49,6 @@
 namespace q8 {
 namespace {
 
-constexpr int kTile = 32;
-constexpr int kBias = 0x4B400000;          // bits of 12582912.0f = 1.5 * 2^23
-constexpr float kBiasF = 12582912.0f;
-
-__device__ __forceinline__ int tile_row(int r, int half) {
-    return 8 * (r / 4) + 4 * half + (r % 4);
-}
-
-__device__ __forceinline__ float2 ws_pair(float ws) {
-    const float hi = __int_as_float(__float_as_int(ws) & ~3);
-    return make_float2(hi, hi * -kBiasF);
-}
 
 // ---------------------------------------------------------------- staged
 
@@ -77,12 +66,6 @@ constexpr int kRing = 3;                        // LDS stages; loads run two sta
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit dwords (gfx9 family)
 constexpr int kNoRead = 0x7FFFFFF0;             // voffset past every range: the load returns 0
 
-// LDS row r holds its eight 16-byte chunks permuted: logical chunk c sits at
-// physical chunk c ^ swz(r).  Sixteen consecutive rows read at the same
-// logical chunk then hit sixteen distinct 16-byte bank groups (with 32 or 64
-// four-byte banks), so the MFMA fragment reads are conflict-free.  swz only
-// depends on r mod 16, so a lane's chunk is the same in every 16-row group.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 constexpr int kWSRows = 256;  // weight-scale rows per block in LDS (BN padded to whole loads)
 
@@ -483,79 +466,6 @@ hipError_t launch_staged(const int8_t* A, const float* AS, const int8_t* W, cons
     return launch_staged_v<TN, PARTIALS, false>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
-// ---------------------------------------------------------------- simple
-
-constexpr int kSimpleWaves = 4;  // waves per workgroup, side by side along N
-
-template <bool PARTIALS>
-__global__ void __launch_bounds__(kSimpleWaves * kWave)
-qgemm_simple_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
-                    const int8_t* __restrict__ W, const float* __restrict__ WS,
-                    float* __restrict__ C, int32_t* __restrict__ P, int M, int N, int K,
-                    int n_groups) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
-    const int64_t i0 = (int64_t)(blockIdx.x / n_groups) * kTile;
-    const int j0 = ((blockIdx.x % n_groups) * kSimpleWaves + wv) * kTile;
-    if (j0 >= N) return;  // whole wave
-    const int KB = K / kBlock;
-    const int half = lane / 32;
-    const int64_t ra = i0 + (lane & 31);
-    const int rw = j0 + (lane & 31);
-    const bool a_ok = ra < M;
-    const bool w_ok = rw < N;
-    const int8_t* Ap = A + ra * K + 16 * half;
-    const int8_t* Wp = W + (int64_t)rw * K + 16 * half;
-    v16i bias;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) bias[r] = PARTIALS ? 0 : kBias;
-
-    float acc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-
-    for (int b = 0; b < KB; ++b) {
-        const v4i af = a_ok ? load16(Ap + (int64_t)kBlock * b) : v4i{0, 0, 0, 0};
-        const v4i wf = w_ok ? load16(Wp + (int64_t)kBlock * b) : v4i{0, 0, 0, 0};
-        const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
-        if constexpr (PARTIALS) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t i = i0 + tile_row(r, half);
-                if (i < M && w_ok) P[(i * N + rw) * KB + b] = d[r];
-            }
-        } else {
-            const float2 wp = ws_pair(w_ok ? WS[(int64_t)rw * KB + b] : 0.0f);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t i = i0 + tile_row(r, half);
-                const float as = i < M ? AS[i * KB + b] : 0.0f;
-                const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
-                acc[r] = fmaf(as, u, acc[r]);
-            }
-        }
-    }
-    if constexpr (!PARTIALS) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t i = i0 + tile_row(r, half);
-            if (i < M && w_ok) C[i * N + rw] = acc[r];
-        }
-    }
-}
-
-template <bool PARTIALS>
-hipError_t launch_simple(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    const int n_groups = (N + kTile * kSimpleWaves - 1) / (kTile * kSimpleWaves);
-    const int64_t m_tiles = (M + kTile - 1) / kTile;
-    const int64_t blocks = m_tiles * n_groups;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    qgemm_simple_kernel<PARTIALS><<<dim3((unsigned)blocks), kSimpleWaves * kWave, 0, stream>>>(
-        A, AS, W, WS, C, P, M, N, K, n_groups);
-    return hipGetLastError();
-}
-
 constexpr int kStagedTN = 7;  // 128 x 224 tiles: 512 x 14336 is exactly 256 of them
 
 }  // namespace
@@ -575,8 +485,7 @@ hipError_t launch_qgemm(const int8_t* A, const float* AS, const int8_t* W, const
         if (P != nullptr) return launch_staged<kStagedTN, true>(A, AS, W, WS, C, P, M, N, K, stream);
         return launch_staged<kStagedTN, false>(A, AS, W, WS, C, P, M, N, K, stream);
     }
-    if (P != nullptr) return launch_simple<true>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_simple<false>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_qgemm_ksplit(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 }  // namespace q8

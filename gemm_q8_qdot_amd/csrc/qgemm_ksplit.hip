@@ -1,0 +1,289 @@
+// Q8_0 block GEMM for few output tiles (small M, or small M x N) on CDNA4
+// int8 MFMA: one workgroup per 32 x 32 output tile, the contraction split
+// across the workgroup's waves.
+//
+// What is computed: the qdot_t row of the Q8_0 table ("Phobos Language Spec",
+// section "Quantized built-ins"), C[i, j] = sum_b AS[i, b] WS[j, b] P[i, j, b],
+// with P the exact int32 block sums ("Quantized built-ins and formats",
+// section "Q8_0": the inner sum is taken in integers).
+//
+// Why this shape: with M = 64 and N = 4096 there are only 2 x 128 output
+// tiles of 32 x 32, so a tile per wave leaves most SIMDs idle and makes each
+// wave walk all K/32 blocks serially.  Here a workgroup of NW waves owns one
+// tile and wave w takes a contiguous range of chunks of four Q8_0 blocks
+// (128 k).  Per chunk a wave
+//   - loads the tile's 32 A rows and 32 W rows, 128 contiguous bytes of each
+//     (eight lanes per row, eight rows per 16-byte load instruction: the
+//     MFMA operand layout itself would touch 32 rows per instruction, which
+//     the memory pipeline serves about three times slower), and the 32 x 4
+//     activation and weight scales (four lanes per row);
+//   - writes them to its own LDS area (rows swizzled so that the fragment
+//     reads are bank-conflict-free) and reads them back in MFMA layout: an
+//     exchange inside one wave, ordered by the LDS queue of that wave;
+//   - per block one v_mfma_i32_32x32x32_i8 (one Q8_0 block) seeded with the
+//     f32 bias pattern, then the 2-op f32 epilogue of ws_pair.
+// Sixteen waves per workgroup (four per SIMD) hide the load latency; the
+// register double-buffered variant (Q8_KS_PREFETCH=1) needs more VGPRs than
+// four waves per SIMD allow and measured slower on MI355X.  At the end the NW partial tiles are summed in LDS in wave order (a fixed
+// order: the result is deterministic) and stored.  Tiles sharing a W slab
+// (the M tiles of one N tile) get consecutive launch slots of one XCD so the
+// slab is read from HBM once.
+#include "q8_device.h"
+#include "q8_launch.h"
+
+namespace q8 {
+namespace {
+
+#ifndef Q8_KS_WAVES
+#define Q8_KS_WAVES 16
+#endif
+#ifndef Q8_KS_PREFETCH
+#define Q8_KS_PREFETCH 0
+#endif
+
+constexpr int kKsWaves = Q8_KS_WAVES;  // waves per workgroup (K split)
+constexpr int kKsBlocks = 4;           // Q8_0 blocks per chunk
+constexpr int kKsSeg = kKsBlocks * kBlock;  // 128 bytes of a row per chunk
+
+// One wave's staging area for one chunk.
+struct KsStage {
+    int8_t a[kTile * kKsSeg];       // [row][8 chunks of 16 B], swizzled
+    int8_t w[kTile * kKsSeg];
+    float as[kKsBlocks][kTile];     // [block][A row]
+    float ws[kTile][kKsBlocks];     // [W row][block]
+};
+
+template <int NW>
+constexpr size_t ksplit_smem_bytes() {
+    // The partial tiles of the final reduction ([NW][16][64] floats) reuse
+    // the staging areas once every wave is done with them.
+    constexpr size_t stage = NW * sizeof(KsStage);
+    constexpr size_t red = (size_t)NW * 16 * kWave * sizeof(float);
+    return stage > red ? stage : red;
+}
+
+// A chunk's operands as loaded: lane l holds 16 bytes of rows 8q + l/8
+// (q = 0..3), chunk l % 8, and the scales of rows l/4 and 16 + l/4,
+// block l % 4.
+struct KsRaw {
+    v4i a[4], w[4];
+    float as[2], ws[2];
+};
+
+template <int NW, bool PF, bool PARTIALS>
+__global__ void __launch_bounds__(NW * kWave)
+qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
+                    const int8_t* __restrict__ W, const float* __restrict__ WS,
+                    float* __restrict__ C, int32_t* __restrict__ P, int M, int N, int K,
+                    int m_tiles, int tiles_total) {
+    extern __shared__ __align__(16) int8_t ks_smem[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    // The 8 XCDs take workgroups round-robin: consecutive tiles (the M tiles
+    // of one N tile) go to consecutive slots of one XCD.
+    int tile = blockIdx.x;
+    if (tiles_total % 8 == 0) tile = (blockIdx.x % 8) * (tiles_total / 8) + blockIdx.x / 8;
+    const int64_t i0 = (int64_t)(tile % m_tiles) * kTile;
+    const int64_t j0 = (int64_t)(tile / m_tiles) * kTile;
+    const int KB = K / kBlock;
+    KsStage& st = reinterpret_cast<KsStage*>(ks_smem)[wv];
+
+    // ---- load-side lane roles
+    const int lrow = lane / 8;   // row within an 8-row load group
+    const int lch = lane % 8;    // 16-byte chunk of the 128-byte segment
+    const int srow = lane / 4;   // scale row (and 16 + srow)
+    const int sblk = lane % 4;   // scale block within the chunk
+    const int8_t* a_src[4];
+    const int8_t* w_src[4];
+    bool a_ok[4], w_ok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t ia = i0 + 8 * q + lrow;
+        const int64_t jw = j0 + 8 * q + lrow;
+        a_ok[q] = ia < M;
+        w_ok[q] = jw < N;
+        a_src[q] = A + (a_ok[q] ? ia * K : 0) + 16 * lch;
+        w_src[q] = W + (w_ok[q] ? jw * K : 0) + 16 * lch;
+    }
+    bool as_ok[2], ws_ok[2];
+    const float* as_src[2];
+    const float* ws_src[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int64_t ia = i0 + 16 * k + srow;
+        const int64_t jw = j0 + 16 * k + srow;
+        as_ok[k] = !PARTIALS && ia < M;
+        ws_ok[k] = !PARTIALS && jw < N;
+        as_src[k] = AS + (as_ok[k] ? ia * KB : 0) + sblk;
+        ws_src[k] = WS + (ws_ok[k] ? jw * KB : 0) + sblk;
+    }
+
+    // ---- MFMA-side lane roles
+    const int half = lane / 32;
+    const int r32 = lane & 31;
+    int frag_off[kKsBlocks];  // logical chunk 2 t + half of row r32
+#pragma unroll
+    for (int t = 0; t < kKsBlocks; ++t) frag_off[t] = r32 * kKsSeg + 16 * ((2 * t + half) ^ swz(r32));
+
+    auto load_chunk = [&](KsRaw& raw, int c) {
+        const int kb0 = c * kKsBlocks;
+        const bool seg_ok = kb0 + lch / 2 < KB;  // this lane's 16 bytes are inside K
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t off = (int64_t)kb0 * kBlock;
+            raw.a[q] = (a_ok[q] && seg_ok) ? load16(a_src[q] + off) : v4i{0, 0, 0, 0};
+            raw.w[q] = (w_ok[q] && seg_ok) ? load16(w_src[q] + off) : v4i{0, 0, 0, 0};
+        }
+        if constexpr (!PARTIALS) {
+            const bool blk_ok = kb0 + sblk < KB;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                raw.as[k] = (as_ok[k] && blk_ok) ? as_src[k][kb0] : 0.0f;
+                raw.ws[k] = (ws_ok[k] && blk_ok) ? ws_src[k][kb0] : 0.0f;
+            }
+        }
+    };
+
+    v16i bias;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bias[r] = PARTIALS ? 0 : kBias;
+    asm volatile("" : "+v"(bias));
+
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+
+    auto stage_and_compute = [&](const KsRaw& raw, int c) {
+        // Lanes exchange data through this wave's LDS area: keep the compiler
+        // from moving LDS accesses across the write/read boundaries (the LDS
+        // queue itself serves one wave's accesses in order).
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = 8 * q + lrow;
+            const int off = row * kKsSeg + 16 * (lch ^ swz(row));
+            *reinterpret_cast<v4i*>(st.a + off) = raw.a[q];
+            *reinterpret_cast<v4i*>(st.w + off) = raw.w[q];
+        }
+        if constexpr (!PARTIALS) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                st.as[sblk][16 * k + srow] = raw.as[k];
+                st.ws[16 * k + srow][sblk] = raw.ws[k];
+            }
+        }
+        asm volatile("" ::: "memory");
+        const int kb0 = c * kKsBlocks;
+        float4 ws4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if constexpr (!PARTIALS) ws4 = *reinterpret_cast<const float4*>(&st.ws[r32][0]);
+        const float wsv[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
+#pragma unroll
+        for (int t = 0; t < kKsBlocks; ++t) {
+            const int b = kb0 + t;
+            if (b >= KB) continue;  // wave-uniform
+            const v4i af = *reinterpret_cast<const v4i*>(st.a + frag_off[t]);
+            const v4i wf = *reinterpret_cast<const v4i*>(st.w + frag_off[t]);
+            const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
+            if constexpr (PARTIALS) {
+                const int64_t j = j0 + r32;
+                if (j < N) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t i = i0 + tile_row(r, half);
+                        if (i < M) P[(i * N + j) * KB + b] = d[r];
+                    }
+                }
+            } else {
+                const float2 wp = ws_pair(wsv[t]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // rows 8q + 4 half + 0..3 of the tile: one 16-byte LDS read
+                    const float4 a4 = *reinterpret_cast<const float4*>(&st.as[t][8 * q + 4 * half]);
+                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * q + e;
+                        const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
+                        acc[r] = fmaf(av[e], u, acc[r]);
+                    }
+                }
+            }
+        }
+    };
+
+    const int nchunks = (KB + kKsBlocks - 1) / kKsBlocks;
+    const int per_wave = (nchunks + NW - 1) / NW;
+    const int c_begin = wv * per_wave;
+    const int c_end = min(c_begin + per_wave, nchunks);
+    if constexpr (PF) {
+        KsRaw r0, r1;
+        if (c_begin < c_end) load_chunk(r0, c_begin);
+        for (int c = c_begin; c < c_end; c += 2) {
+            if (c + 1 < c_end) load_chunk(r1, c + 1);
+            stage_and_compute(r0, c);
+            if (c + 1 >= c_end) break;
+            if (c + 2 < c_end) load_chunk(r0, c + 2);
+            stage_and_compute(r1, c + 1);
+        }
+    } else {
+        for (int c = c_begin; c < c_end; ++c) {
+            KsRaw r0;
+            load_chunk(r0, c);
+            stage_and_compute(r0, c);
+        }
+    }
+
+    if constexpr (!PARTIALS) {
+        // Sum the NW partial tiles in wave order and store the tile.
+        float* red = reinterpret_cast<float*>(ks_smem);  // [NW][16][64], over the stages
+        __syncthreads();  // every wave is done with its staging area
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(wv * 16 + r) * kWave + lane] = acc[r];
+        __syncthreads();
+        for (int o = threadIdx.x; o < 16 * kWave; o += NW * kWave) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) s += red[w * 16 * kWave + o];
+            const int r = o / kWave;
+            const int l = o % kWave;
+            const int64_t i = i0 + tile_row(r, l / 32);
+            const int64_t j = j0 + (l & 31);
+            if (i < M && j < N) C[i * N + j] = s;
+        }
+    }
+}
+
+template <int NW, bool PF, bool PARTIALS>
+hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                     float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    const int64_t m_tiles = (M + kTile - 1) / kTile;
+    const int64_t n_tiles = (N + kTile - 1) / kTile;
+    const int64_t total = m_tiles * n_tiles;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    constexpr size_t smem = ksplit_smem_bytes<NW>();
+    static_assert(smem <= 160 * 1024, "LDS budget");
+    auto kern = qgemm_ksplit_kernel<NW, PF, PARTIALS>;
+    if (smem > 64 * 1024) {
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+    }
+    kern<<<dim3((unsigned)total), NW * kWave, smem, stream>>>(A, AS, W, WS, C, P, M, N, K,
+                                                             (int)m_tiles, (int)total);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                               float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    constexpr bool pf = Q8_KS_PREFETCH != 0;
+    if (P != nullptr) return launch_ks<kKsWaves, pf, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks<kKsWaves, pf, false>(A, AS, W, WS, C, P, M, N, K, stream);
+}
+
+}  // namespace q8

@@ -85,9 +85,10 @@ int q8_qdot_partials(const int8_t *A, const int8_t *W, int32_t *P,
 
 /*
  * The kernel a shape dispatches to: 0 = wave64 matvec (M < 8; one A row per
- * grid row); for M >= 8 the int8-MFMA block GEMM, 1 = per-wave 32 x 32 tiles
- * read straight from global memory (small M or N), 2 = LDS-staged 128 x 224
- * workgroup tiles (large M and N).  Q8_EINVAL for bad shapes.
+ * grid row); for M >= 8 the int8-MFMA block GEMM, 1 = one workgroup per
+ * 32 x 32 output tile with the K/32 blocks split across its waves (few
+ * tiles: small M or N), 2 = LDS-staged 128 x 224 workgroup tiles (large M
+ * and N).  Q8_EINVAL for bad shapes.
  */
 int q8_qdot_path(int M, int N, int K);
 

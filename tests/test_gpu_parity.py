@@ -131,7 +131,7 @@ EDGE = [
     (1, 1, 32), (1, 37, 1056), (2, 100, 32), (3, 129, 2080), (5, 64, 4096), (7, 300, 1024),
     (8, 1, 64), (9, 37, 96), (16, 33, 128), (31, 65, 1056), (33, 100, 4096), (63, 129, 320),
     (64, 4096, 32), (65, 224, 2048), (128, 449, 512), (1, 513, 16416), (3, 8, 32800),
-    (12, 70, 16416), (4, 4099, 14336), (9, 1, 14336),
+    (12, 70, 16416), (4, 4099, 14336), (9, 1, 14336), (127, 300, 4160), (40, 2050, 8224),
 ]
 
 
