@@ -88,6 +88,22 @@ __device__ __forceinline__ float2 ws_pair(float ws) {
     return make_float2(hi, hi * -kBiasF);
 }
 
+// ---- raw buffer loads (SGPR resource + 32-bit per-lane offset) ----
+// A load whose per-lane offset is at or past the resource's byte count
+// returns zeros; kNoRead is such an offset for every resource here.
+constexpr int kNoRead = 0x7FFFFFF0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+__device__ __forceinline__ v4i buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 // LDS tiles of 128-byte row segments (four Q8_0 blocks = eight 16-byte
 // chunks per row): row r holds its chunks permuted, logical chunk c at
 // physical chunk c ^ swz(r).  Sixteen consecutive rows read at the same

@@ -47,6 +47,8 @@ int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
         if (!aligned(C, 4)) return Q8_EALIGN;
         return status_of(q8::launch_fill_zero(C, (int64_t)M * N, stream));
     }
+    // The block GEMMs address a 32-row operand tile with 32-bit offsets.
+    if (M > kMatvecMaxM && (int64_t)K * 32 > INT32_MAX) return Q8_ERANGE;
     if (A == nullptr || W == nullptr) return Q8_ENULL;
     if (!partials && (AS == nullptr || WS == nullptr || C == nullptr)) return Q8_ENULL;
     if (!aligned(A, 16) || !aligned(W, 16)) return Q8_EALIGN;

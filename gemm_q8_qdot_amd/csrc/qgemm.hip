@@ -54,9 +54,9 @@ namespace {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kMWaves = 4;                      // along M, 32 rows each
-constexpr int kNWaves = 2;                      // along N: tiles 0..3 and 4..TN-1
-constexpr int kStagedWaves = kMWaves * kNWaves; // 8 waves: two per SIMD
+constexpr int kMWaves = 4;                      // along M: one 32-row strip per SIMD
+constexpr int kNGroups = 4;                     // along N: tiles {0,1} {2,3} {4,5} {6}
+constexpr int kStagedWaves = kMWaves * kNGroups;  // 16 waves: four per SIMD
 constexpr int kStagedThreads = kStagedWaves * kWave;
 constexpr int kBM = kMWaves * kTile;            // 128 rows of A per workgroup
 constexpr int kSB = 4;                          // Q8_0 blocks per stage
@@ -64,9 +64,6 @@ constexpr int kSeg = kSB * kBlock;              // 128 bytes of a row per stage
 constexpr int kRowsPerLoad = kWave * 16 / kSeg; // one 16-byte-per-lane load: 8 rows
 constexpr int kRing = 3;                        // LDS stages; loads run two stages ahead
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit dwords (gfx9 family)
-constexpr int kNoRead = 0x7FFFFFF0;             // voffset past every range: the load returns 0
-
-
 constexpr int kWSRows = 256;  // weight-scale rows per block in LDS (BN padded to whole loads)
 
 template <int TN>
@@ -117,6 +114,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // and each weight-scale row's 4 block scales come as one 16-byte load
 // (LDS layout [row][block]); otherwise one dword per (block, row) with
 // blocks past K read as 0 (layout [block][row]).
+//
+// Wave roles: wave wv runs on SIMD wv % 4 (waves are placed round-robin)
+// and computes the 32 activation rows 32 (wv % 4) .. against tiles
+// {2g, 2g + 1} (g = wv / 4 < 3) or {6} (g = 3) of the 7 weight tiles, for
+// every block: four waves per SIMD keep the VALU epilogue of one wave going
+// while another waits on its MFMA or LDS reads, and every output tile has a
+// single owner (no cross-wave reduction).
 template <int TN, bool PARTIALS, bool WSX4>
 __global__ void __launch_bounds__(kStagedThreads, 1)
 qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
@@ -124,20 +128,27 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     float* __restrict__ C, int32_t* __restrict__ P, int M, int N, int K,
                     int tiles_m, int tiles_total) {
     constexpr int BN = TN * kTile;
+    static_assert(TN == 7, "tile groups {0,1} {2,3} {4,5} {6}");
     static_assert(BN <= kWSRows, "weight-scale rows");
-    // Loads of one stage ("jobs"), each one wave-wide instruction.  Every
-    // wave has a fixed pattern: A rows 16 wv .. 16 wv + 15 (2 jobs), then its
-    // share of the W rows (4 jobs for waves 0-3, 3 for waves 4-7), then one
-    // activation-scale job (block wv / 2, rows 64 (wv % 2) ..), then weight
-    // scales: with WSX4 one 16-byte job (rows 64 (wv - 4) ..) for waves 4-7,
-    // else two dword jobs per wave (block wv / 2, rows 128 (wv % 2) + 64 k ..).
+    // Loads of one stage ("jobs"), each one wave-wide instruction, four or
+    // five per wave in a fixed pattern (a job a wave does not have is a
+    // dummy load that reads nothing):
+    //   slot 0: A rows 8 wv .. 8 wv + 7
+    //   slot 1: W rows 8 wv ..
+    //   slot 2: W rows 8 (16 + wv) .. for wv < 12; activation-scale job
+    //           2 (wv - 12) for wv >= 12
+    //   slot 3: WSX4: weight-scale job wv for wv < 4, activation-scale job
+    //           2 (wv - 12) + 1 for wv >= 12;  else activation-scale job
+    //           2 (wv - 12) + 1 for wv >= 12, then weight-scale job wv
+    // Activation-scale job e: block e / 2, rows 64 (e % 2) + lane (dword).
+    // Weight-scale job e: WSX4: rows 64 e + lane, blocks 0..3 (16 bytes);
+    // else block e / 4, rows 64 (e % 4) + lane (dword).
     constexpr int kWJobs = BN / kRowsPerLoad;             // 28 for TN = 7
-    static_assert(kBM / kRowsPerLoad == 2 * kStagedWaves, "two A jobs per wave");
-    static_assert(kWJobs == 4 * 4 + 4 * 3, "W jobs: 4 per wave for waves 0-3, 3 for waves 4-7");
-    static_assert(kSB * kBM / kWave == kStagedWaves, "one activation-scale job per wave");
-    static_assert(kWSRows * 16 / 1024 == 4 && kSB * kWSRows / kWave == 2 * kStagedWaves, "weight-scale jobs");
-    // loads per wave per stage (all waves): 2 A + 4 W + activation scales + weight scales
-    constexpr int kLoadsPerWave = PARTIALS ? 6 : (WSX4 ? 8 : 9);
+    static_assert(kBM / kRowsPerLoad == kStagedWaves, "one A job per wave");
+    static_assert(kWJobs == kStagedWaves + 12, "W jobs: two for waves 0-11, one for 12-15");
+    static_assert(kSB * kBM / kWave == 8, "eight activation-scale jobs");
+    static_assert(kWSRows * 16 / 1024 == 4 && kSB * kWSRows / kWave == kStagedWaves, "weight-scale jobs");
+    constexpr int kLoadsPerWave = WSX4 ? 4 : 5;  // loads per wave per stage (all waves)
     extern __shared__ __align__(16) unsigned char smem_raw[];
     StagedStage<TN>* ring = reinterpret_cast<StagedStage<TN>*>(smem_raw);
 
@@ -156,10 +167,10 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-    // Wave wv runs on SIMD wv % 4: the two waves of a SIMD share 32 rows of
-    // A and split the TN column tiles 4 + (TN - 4), so every SIMD does TN tiles.
-    const int mw = wv % kMWaves;      // which 32 rows
-    const int nw = wv / kMWaves;      // tiles 0..3 or 4..TN-1
+    const int mw = wv % kMWaves;      // which 32 activation rows
+    const int g = wv / kMWaves;       // which weight tiles
+    const int t0 = 2 * g;             // first weight tile of this wave
+    const bool two = g < 3;           // second tile (2 g + 1) present
     const int half = lane / 32;
     const int col = lane & 31;
     const int KB = K / kBlock;
@@ -168,8 +179,8 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     // Descriptors of this tile's rows: reads past them return 0.
     const v4i dA = make_desc(A + (int64_t)i0 * K, (int64_t)rows_a * K);
     const v4i dW = make_desc(W + (int64_t)j0 * K, (int64_t)rows_w * K);
-    const v4i dAS = make_desc(AS + (int64_t)i0 * KB, (int64_t)rows_a * KB * 4);
-    const v4i dWS = make_desc(WS + (int64_t)j0 * KB, (int64_t)rows_w * KB * 4);
+    const v4i dAS = make_desc(PARTIALS ? nullptr : AS + (int64_t)i0 * KB, (int64_t)rows_a * KB * 4);
+    const v4i dWS = make_desc(PARTIALS ? nullptr : WS + (int64_t)j0 * KB, (int64_t)rows_w * KB * 4);
 
     // A/W job of rows 8 q' .. 8 q' + 7: lane fills physical chunk lane % 8 of
     // row 8 q' + lane / 8, i.e. reads logical chunk
@@ -180,20 +191,16 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const int voff_even = (lane / 8) * K + 16 * c_even;
     const int voff_odd = (lane / 8) * K + 16 * (c_even ^ 1);
     const int voff_scale = lane * KB * 4;
-    const int w_first = wv < 4 ? 4 * wv : 16 + 3 * (wv - 4);  // first W job of this wave
-    const int w_count = wv < 4 ? 4 : 3;
 
-    // The issue code below has no branches: a load that must not happen
-    // (past the last stage, a wave's missing fourth W job or its missing
-    // weight-scale job) still issues, with voffset kNoRead (reads nothing,
-    // writes zeros) into the spare LDS area past the ring.  Every wave thus
-    // issues the same number of loads per stage, and the math stays one
-    // straight run of code the register allocator handles well.
+    // A job that a wave does not have (or one past the last stage) still
+    // issues, with voffset kNoRead (reads nothing, writes zeros) into the
+    // spare LDS area past the ring: every wave issues the same number of
+    // loads per stage, so one vmcnt wait fits all, and there are no branches.
     uint8_t* spare = smem_raw + sizeof(StagedStage<TN>) * kRing;
 
     // One A/W job (rows 8 qq ..) of stage st; `real` false: a dummy load.
-    auto job_rows = [&](int st, bool is_a, int qq, bool real) {
-        StagedStage<TN>& sg = ring[st % kRing];
+    auto job_rows = [&](int st, int rs, bool is_a, int qq, bool real) {
+        StagedStage<TN>& sg = ring[rs];
         const int kb0 = st * kSB;
         int vo = ((qq & 1) ? voff_odd : voff_even) + qq * kRowsPerLoad * K;
         if constexpr (!WSX4) {  // the last stage may be partial: chunks past K read 0
@@ -207,56 +214,59 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                                : (const void*)spare;
         dma16(is_a ? dA : dW, lds_addr(dst), vo, kb0 * kBlock);
     };
-    // The scale jobs of stage st (none in the debug entry, which has no scales).
-    auto job_scales = [&](int st, bool real) {
-        if constexpr (!PARTIALS) {
-            StagedStage<TN>& sg = ring[st % kRing];
-            const int kb0 = st * kSB;
-            const int blocks_left = KB - kb0;
-            {   // activation scales: block wv / 2, rows 64 (wv % 2) + lane
-                const int sblk = wv / 2, h = wv % 2;
-                const bool ok = real && sblk < blocks_left;
-                const int vo = ok ? voff_scale + h * kWave * KB * 4 + sblk * 4 : kNoRead;
-                dma4(dAS, lds_addr(real ? (const void*)&sg.as[sblk][h * kWave] : (const void*)spare), vo, kb0 * 4);
-            }
-            if constexpr (WSX4) {
-                // waves 4-7: rows 64 e + lane, blocks kb0 .. kb0 + 3 (rows past
-                // the tile read 0); waves 0-3: a dummy load
-                const int e = wv - 4;
-                const bool ok = real && wv >= 4;
-                const int vo = ok ? voff_scale + e * kWave * KB * 4 : kNoRead;
-                dma16(dWS, lds_addr(ok ? (const void*)&sg.ws[e * kWave * kSB] : (const void*)spare), vo, kb0 * 4);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {  // block wv / 2, rows 128 (wv % 2) + 64 k + lane
-                    const int sblk = wv / 2, h = 2 * (wv % 2) + k;
-                    const bool ok = real && sblk < blocks_left;
-                    const int vo = ok ? voff_scale + h * kWave * KB * 4 + sblk * 4 : kNoRead;
-                    dma4(dWS, lds_addr(real ? (const void*)&sg.ws[sblk * kWSRows + h * kWave] : (const void*)spare),
-                         vo, kb0 * 4);
-                }
-            }
-        }
+    // Scale jobs.  A block past K (last stage only) still writes its LDS
+    // slot, with zeros, so the epilogue never reads a stale or uninitialised
+    // scale; the debug entry has no scales and loads none.
+    // Activation-scale job e (block e / 2, rows 64 (e % 2) + lane) of stage st.
+    auto job_as = [&](int st, int rs, int e, bool real) {
+        StagedStage<TN>& sg = ring[rs];
+        const int kb0 = st * kSB;
+        const int sblk = e / 2, h = e % 2;
+        const bool to_slot = real && !PARTIALS;
+        const bool ok = to_slot && sblk < KB - kb0;
+        const int vo = ok ? voff_scale + h * kWave * KB * 4 + sblk * 4 : kNoRead;
+        dma4(dAS, lds_addr(to_slot ? (const void*)&sg.as[sblk][h * kWave] : (const void*)spare), vo, kb0 * 4);
     };
-    // Slice p (0..3) of the loads of stage st: slices go between the four
-    // blocks of math so the load queue never backs up into the math.
-    auto fetch_slice = [&](int st, int p, bool real) {
-        if (p == 0) {
-            job_rows(st, true, 2 * wv, real);
-            job_rows(st, true, 2 * wv + 1, real);
-        } else if (p == 1) {
-            job_rows(st, false, w_first, real);
-            job_rows(st, false, w_first + 1, real);
-        } else if (p == 2) {
-            job_rows(st, false, w_first + 2, real);
-            job_rows(st, false, w_first + 3, real && w_count == 4);
+    // Weight-scale job e of stage st.
+    auto job_ws = [&](int st, int rs, int e, bool real) {
+        StagedStage<TN>& sg = ring[rs];
+        const int kb0 = st * kSB;
+        const bool to_slot = real && !PARTIALS;
+        if constexpr (WSX4) {  // whole stages: every block is inside K
+            const int vo = to_slot ? voff_scale + e * kWave * KB * 4 : kNoRead;
+            dma16(dWS, lds_addr(to_slot ? (const void*)&sg.ws[e * kWave * kSB] : (const void*)spare), vo, kb0 * 4);
         } else {
-            job_scales(st, real);
+            const int sblk = e / 4, h = e % 4;
+            const bool ok = to_slot && sblk < KB - kb0;
+            const int vo = ok ? voff_scale + h * kWave * KB * 4 + sblk * 4 : kNoRead;
+            dma4(dWS, lds_addr(to_slot ? (const void*)&sg.ws[sblk * kWSRows + h * kWave] : (const void*)spare),
+                 vo, kb0 * 4);
         }
     };
-    auto fetch = [&](int st) {
+    // Slot p (0..3) of the loads of stage st (ring slot rs): one slot goes
+    // between two blocks of math, so the load queue never backs up into the
+    // math.
+    auto fetch_slice = [&](int st, int rs, int p, bool real) {
+        if (p == 0) {
+            job_rows(st, rs, true, wv, real);
+        } else if (p == 1) {
+            job_rows(st, rs, false, wv, real);
+        } else if (p == 2) {
+            if (wv < 12) job_rows(st, rs, false, kStagedWaves + wv, real);
+            else job_as(st, rs, 2 * (wv - 12), real);
+        } else {
+            if constexpr (WSX4) {
+                if (wv < 4) job_ws(st, rs, wv, real);
+                else job_as(st, rs, 2 * (wv - 12) + 1, real && wv >= 12);
+            } else {
+                job_as(st, rs, 2 * (wv - 12) + 1, real && wv >= 12);
+                job_ws(st, rs, wv, real);
+            }
+        }
+    };
+    auto fetch = [&](int st, int rs, bool real) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) fetch_slice(st, p, true);
+        for (int p = 0; p < 4; ++p) fetch_slice(st, rs, p, real);
     };
 
     // Fragment read offsets: rows 32 t + col of a tile (swz(32 t + col) =
@@ -271,30 +281,24 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     // Opaque to the optimizer: the tile stays in 16 VGPRs instead of being
     // rebuilt from a scalar before every block.
     asm volatile("" : "+v"(bias));
-    constexpr int kT0 = 4;            // accumulator slots per wave
-    static_assert(TN == 7, "the two waves of a SIMD split 7 tiles as 3 + 3 + (1 split by blocks)");
-    float acc[kT0][16];
+    float acc[2][16];
 #pragma unroll
-    for (int t = 0; t < kT0; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-    // The math of block s (compile-time) of stage st for NT tiles from T0;
-    // wsp[t][s] holds the (ws_hi, bias product) pair of tile t, block s.
-    auto block_math = [&](const StagedStage<TN>& sg, int st, int s, auto nt_const, auto t0_const,
-                          auto slot0_const, const float2 (&wsp)[kT0][kSB]) {
-        constexpr int NT = decltype(nt_const)::value;    // tiles T0 .. T0 + NT - 1
-        constexpr int T0 = decltype(t0_const)::value;
-        constexpr int SL = decltype(slot0_const)::value; // accumulator slot of tile T0
+    // The math of block s of stage st: this wave's one or two tiles.
+    auto block_math = [&](auto nt_const, const StagedStage<TN>& sg, int st, int s) {
+        constexpr int NT = decltype(nt_const)::value;
         const int kb = st * kSB + s;
         const v4i af = *reinterpret_cast<const v4i*>(sg.a + mw * kTile * kSeg + frag_off[s]);
         if constexpr (PARTIALS) {
             if (kb < KB) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (T0 + t) * kTile * kSeg + frag_off[s]);
+                    const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (t0 + t) * kTile * kSeg + frag_off[s]);
                     const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
-                    const int j = j0 + (T0 + t) * kTile + col;
+                    const int j = j0 + (t0 + t) * kTile + col;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int i = i0 + mw * kTile + tile_row(r, half);
@@ -307,45 +311,25 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             // add exactly 0, so there is no per-block branch here.
             float asv[16];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&sg.as[s][mw * kTile + 8 * g + 4 * half]);
-                asv[4 * g + 0] = a4.x;
-                asv[4 * g + 1] = a4.y;
-                asv[4 * g + 2] = a4.z;
-                asv[4 * g + 3] = a4.w;
+            for (int q = 0; q < 4; ++q) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&sg.as[s][mw * kTile + 8 * q + 4 * half]);
+                asv[4 * q + 0] = a4.x;
+                asv[4 * q + 1] = a4.y;
+                asv[4 * q + 2] = a4.z;
+                asv[4 * q + 3] = a4.w;
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (T0 + t) * kTile * kSeg + frag_off[s]);
+                const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (t0 + t) * kTile * kSeg + frag_off[s]);
                 const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
-                const float2 wp = wsp[SL + t][s];
+                // the (ws_hi, bias product) pair of this lane's weight row
+                const int wrow = (t0 + t) * kTile + col;
+                const float2 wp = ws_pair(WSX4 ? sg.ws[wrow * kSB + s] : sg.ws[s * kWSRows + wrow]);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
-                    acc[SL + t][r] = fmaf(asv[r], u, acc[SL + t][r]);
+                    acc[t][r] = fmaf(asv[r], u, acc[t][r]);
                 }
-            }
-        }
-    };
-    // The weight-scale pairs of this wave's NT tiles for the whole stage
-    // (one 16-byte read per tile in the [row][block] layout: conflict-free).
-    auto load_wsp = [&](const StagedStage<TN>& sg, auto nt_const, auto t0_const, float2 (&wsp)[kT0][kSB]) {
-        constexpr int NT = decltype(nt_const)::value;    // slots 0 .. NT-1 = tiles T0 ..
-        constexpr int T0 = decltype(t0_const)::value;
-        if constexpr (!PARTIALS) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int wrow = (T0 + t) * kTile + col;
-                float w4[kSB];
-                if constexpr (WSX4) {
-                    const float4 v = *reinterpret_cast<const float4*>(&sg.ws[wrow * kSB]);
-                    w4[0] = v.x; w4[1] = v.y; w4[2] = v.z; w4[3] = v.w;
-                } else {
-#pragma unroll
-                    for (int s = 0; s < kSB; ++s) w4[s] = sg.ws[s * kWSRows + wrow];
-                }
-#pragma unroll
-                for (int s = 0; s < kSB; ++s) wsp[t][s] = ws_pair(w4[s]);
             }
         }
     };
@@ -353,82 +337,61 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     // Stage st + 1 has landed once at most this wave's kLoadsPerWave newest
     // loads (those of stage st + 2) are outstanding (loads complete in order).
     auto wait_vmcnt_stage = [&]() {
-        if constexpr (kLoadsPerWave == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-        else if constexpr (kLoadsPerWave == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        if constexpr (kLoadsPerWave == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     };
 
     // Prologue: stages 0 and 1 in flight, stage 0 complete.
-    fetch(0);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) fetch_slice(1, p, nstages > 1);
+    fetch(0, 0, true);
+    fetch(1, 1, nstages > 1);
     wait_vmcnt_stage();
     __builtin_amdgcn_s_barrier();
 
-    for (int st = 0; st < nstages; ++st) {
-        const bool ahead = st + 2 < nstages;
-        const StagedStage<TN>& sg = ring[st % kRing];
-        // Loads of stage st + 2 (two ahead), interleaved with this stage's math.
-        // Tiles: wave nw = 0 owns 0, 1, 2 and blocks 0, 1 of tile 3 (slot 3);
-        // nw = 1 owns 4, 5, 6 (slots 1-3) and blocks 2, 3 of tile 3 (slot 0):
-        // 14 tile-blocks each per stage.
-        float2 wsp[kT0][kSB];
-        if (nw == 0) {
-            load_wsp(sg, std::integral_constant<int, 4>(), std::integral_constant<int, 0>(), wsp);
+    // The stage loop and the stores, for a wave with NT (1 or 2) tiles: one
+    // straight run of code per case (a branch per tile inside the loop makes
+    // the register allocator spill).
+    auto run = [&](auto nt_const) {
+        constexpr int NT = decltype(nt_const)::value;
+        int rs = 0;  // ring slot of stage st; stage st + 2 goes to the slot before it
+        for (int st = 0; st < nstages; ++st) {
+            const bool ahead = st + 2 < nstages;
+            const int rs2 = rs == 0 ? kRing - 1 : rs - 1;
+            const StagedStage<TN>& sg = ring[rs];
+            // The loads of stage st + 2 (two ahead) go between this stage's blocks.
 #pragma unroll
             for (int s = 0; s < kSB; ++s) {
-                fetch_slice(st + 2, s, ahead);
-                if (s < 2)
-                    block_math(sg, st, s, std::integral_constant<int, 4>(), std::integral_constant<int, 0>(),
-                               std::integral_constant<int, 0>(), wsp);
-                else
-                    block_math(sg, st, s, std::integral_constant<int, 3>(), std::integral_constant<int, 0>(),
-                               std::integral_constant<int, 0>(), wsp);
+                fetch_slice(st + 2, rs2, s, ahead);
+                block_math(nt_const, sg, st, s);
+                // Pin the accumulators here: without it the compiler sinks
+                // the epilogues of all four blocks below the last MFMA and
+                // holds 16 VGPRs per pending MFMA result (spills).
+                if constexpr (!PARTIALS)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 4)
+                        asm volatile("" : "+v"(acc[t][r]), "+v"(acc[t][r + 1]), "+v"(acc[t][r + 2]),
+                                     "+v"(acc[t][r + 3]));
             }
-        } else {
-            load_wsp(sg, std::integral_constant<int, 4>(), std::integral_constant<int, 3>(), wsp);
-#pragma unroll
-            for (int s = 0; s < kSB; ++s) {
-                fetch_slice(st + 2, s, ahead);
-                if (s < 2)
-                    block_math(sg, st, s, std::integral_constant<int, 3>(), std::integral_constant<int, 4>(),
-                               std::integral_constant<int, 1>(), wsp);
-                else
-                    block_math(sg, st, s, std::integral_constant<int, 4>(), std::integral_constant<int, 3>(),
-                               std::integral_constant<int, 0>(), wsp);
-            }
+            wait_vmcnt_stage();
+            // Bare barrier (no fence): the loads of stage st + 2 stay in flight.
+            __builtin_amdgcn_s_barrier();
+            rs = rs == kRing - 1 ? 0 : rs + 1;
         }
-        wait_vmcnt_stage();
-        // Bare barrier (no fence): the loads of stage st + 2 stay in flight.
-        __builtin_amdgcn_s_barrier();
-    }
-
-    if constexpr (!PARTIALS) {
-        // Tile 3 = (blocks 0, 1 of every stage, wave nw = 0) + (blocks 2, 3,
-        // wave nw = 1), added in this fixed order (deterministic).
-        float* red = reinterpret_cast<float*>(smem_raw) + (size_t)mw * 16 * kWave;
-        if (nw == 1) {
+        if constexpr (!PARTIALS) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[r * kWave + lane] = acc[0][r];
-        }
-        __syncthreads();
-        if (nw == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[3][r] += red[r * kWave + lane];
-        }
-        const int tb = nw == 0 ? 0 : 3;  // tile of slot 0
-#pragma unroll
-        for (int sl = 0; sl < kT0; ++sl) {
-            if (nw == 0 || sl > 0) {
-                const int j = j0 + (tb + sl) * kTile + col;
+            for (int t = 0; t < NT; ++t) {
+                const int j = j0 + (t0 + t) * kTile + col;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = i0 + mw * kTile + tile_row(r, half);
-                    if (i < M && j < N) C[(int64_t)i * N + j] = acc[sl][r];
+                    if (i < M && j < N) C[(int64_t)i * N + j] = acc[t][r];
                 }
             }
         }
-    }
+    };
+    if (two) run(std::integral_constant<int, 2>());
+    else run(std::integral_constant<int, 1>());
 }
 
 template <int TN, bool PARTIALS, bool WSX4>
@@ -439,7 +402,7 @@ hipError_t launch_staged_v(const int8_t* A, const float* AS, const int8_t* W, co
     const int64_t tiles_n = (N + BN - 1) / BN;
     const int64_t total = tiles_m * tiles_n;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    // More than half of the CU's 160 KiB LDS: exactly one workgroup (two
+    // More than half of the CU's 160 KiB LDS: exactly one workgroup (four
     // waves per SIMD) per CU.
     constexpr size_t need = staged_smem_bytes<TN>();
     constexpr size_t smem = need > 82 * 1024 ? need : 82 * 1024;

@@ -88,35 +88,22 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const int KB = K / kBlock;
     KsStage& st = reinterpret_cast<KsStage*>(ks_smem)[wv];
 
-    // ---- load-side lane roles
+    // ---- load-side lane roles.  Raw buffer loads: rows past M or N fall
+    // outside the resource and read as zero; the row part of every offset is
+    // in the per-lane offset, the chunk's k offset in the scalar one.
     const int lrow = lane / 8;   // row within an 8-row load group
     const int lch = lane % 8;    // 16-byte chunk of the 128-byte segment
     const int srow = lane / 4;   // scale row (and 16 + srow)
     const int sblk = lane % 4;   // scale block within the chunk
-    const int8_t* a_src[4];
-    const int8_t* w_src[4];
-    bool a_ok[4], w_ok[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int64_t ia = i0 + 8 * q + lrow;
-        const int64_t jw = j0 + 8 * q + lrow;
-        a_ok[q] = ia < M;
-        w_ok[q] = jw < N;
-        a_src[q] = A + (a_ok[q] ? ia * K : 0) + 16 * lch;
-        w_src[q] = W + (w_ok[q] ? jw * K : 0) + 16 * lch;
-    }
-    bool as_ok[2], ws_ok[2];
-    const float* as_src[2];
-    const float* ws_src[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int64_t ia = i0 + 16 * k + srow;
-        const int64_t jw = j0 + 16 * k + srow;
-        as_ok[k] = !PARTIALS && ia < M;
-        ws_ok[k] = !PARTIALS && jw < N;
-        as_src[k] = AS + (as_ok[k] ? ia * KB : 0) + sblk;
-        ws_src[k] = WS + (ws_ok[k] ? jw * KB : 0) + sblk;
-    }
+    const int rows_a = M - i0 < kTile ? (int)(M - i0) : kTile;
+    const int rows_w = N - j0 < kTile ? (int)(N - j0) : kTile;
+    const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A + i0 * K, (int64_t)rows_a * K);
+    const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(W + j0 * K, (int64_t)rows_w * K);
+    // (the debug entry passes no scales and reads none)
+    const __amdgpu_buffer_rsrc_t rAS = buffer_rsrc(PARTIALS ? nullptr : AS + i0 * KB, (int64_t)rows_a * KB * 4);
+    const __amdgpu_buffer_rsrc_t rWS = buffer_rsrc(PARTIALS ? nullptr : WS + j0 * KB, (int64_t)rows_w * KB * 4);
+    const int voff_ops = lrow * K + 16 * lch;             // + 8 q K for group q
+    const int voff_sc = (srow * KB + sblk) * 4;           // + 16 k KB * 4 for half k
 
     // ---- MFMA-side lane roles
     const int half = lane / 32;
@@ -127,19 +114,22 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 
     auto load_chunk = [&](KsRaw& raw, int c) {
         const int kb0 = c * kKsBlocks;
-        const bool seg_ok = kb0 + lch / 2 < KB;  // this lane's 16 bytes are inside K
+        // a lane whose 16 bytes lie past K reads nothing (zeros)
+        const int vo = (kb0 + lch / 2 < KB) ? voff_ops : kNoRead;
+        const int so = kb0 * kBlock;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t off = (int64_t)kb0 * kBlock;
-            raw.a[q] = (a_ok[q] && seg_ok) ? load16(a_src[q] + off) : v4i{0, 0, 0, 0};
-            raw.w[q] = (w_ok[q] && seg_ok) ? load16(w_src[q] + off) : v4i{0, 0, 0, 0};
+            const int v = vo == kNoRead ? kNoRead : vo + 8 * q * K;
+            raw.a[q] = buffer_load16(rA, v, so);
+            raw.w[q] = buffer_load16(rW, v, so);
         }
         if constexpr (!PARTIALS) {
-            const bool blk_ok = kb0 + sblk < KB;
+            const int vs = (kb0 + sblk < KB) ? voff_sc : kNoRead;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                raw.as[k] = (as_ok[k] && blk_ok) ? as_src[k][kb0] : 0.0f;
-                raw.ws[k] = (ws_ok[k] && blk_ok) ? ws_src[k][kb0] : 0.0f;
+                const int v = vs == kNoRead ? kNoRead : vs + 16 * k * KB * 4;
+                raw.as[k] = buffer_load_f32(rAS, v, kb0 * 4);
+                raw.ws[k] = buffer_load_f32(rWS, v, kb0 * 4);
             }
         }
     };

@@ -58,7 +58,8 @@ typedef enum {
     Q8_EINVAL = -1,  /* M, N or K negative, or K % 32 != 0 */
     Q8_ENULL = -2,   /* a pointer the call must dereference is NULL */
     Q8_EALIGN = -3,  /* A/W/X/Q not 16-byte aligned, or another array not 4-byte aligned */
-    Q8_ERANGE = -4,  /* an extent product overflows 64-bit byte addressing */
+    Q8_ERANGE = -4,  /* an extent product overflows 64-bit byte addressing, or
+                        M >= 8 with 32 * K > 2^31 - 1 (32-bit tile offsets) */
     Q8_ELAUNCH = -5  /* the HIP runtime rejected the launch (hipGetLastError) */
 } q8_status;
 

@@ -112,6 +112,10 @@ def test_empty_outputs_are_noops(lib):
 def test_range_overflow_rejected(lib):
     big = 2**31 - 32
     assert q8.q8_qdot_partials_raw(16, 16, 16, big, big, big) == q8.Q8_ERANGE
+    # the block GEMMs (M >= 8) need 32 * K < 2^31; the matvec does not
+    huge_k = 2**26
+    assert q8.q8_qdot_raw(16, 16, 16, 16, 16, 8, 4, huge_k) == q8.Q8_ERANGE
+    assert q8.q8_qdot_partials_raw(16, 16, 16, 8, 4, huge_k) == q8.Q8_ERANGE
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
