@@ -77,6 +77,10 @@ def _load():
             lib.q8o_qdot_f64.argtypes = [p, p, p, p, i64, i64, i64, p, p]
             lib.q8o_qdot_f64_at.restype = ctypes.c_int
             lib.q8o_qdot_f64_at.argtypes = [p, p, p, p, i64, i64, i64, p, p, i64, p, p]
+            lib.q8o_qmma_f64.restype = ctypes.c_int
+            lib.q8o_qmma_f64.argtypes = [p, p, p, p, i64, i64, i64, p, p]
+            lib.q8o_qmma_f64_at.restype = ctypes.c_int
+            lib.q8o_qmma_f64_at.argtypes = [p, p, p, p, i64, i64, i64, p, p, i64, p, p]
             lib.q8o_block_partials_at.restype = ctypes.c_int
             lib.q8o_block_partials_at.argtypes = [p, p, i64, i64, i64, p, p, i64, p]
             _lib = lib
@@ -180,6 +184,50 @@ def qdot_f64_at(A, AS, W, WS, ii, jj):
                                 _ptr(ii), _ptr(jj), ii.shape[0], _ptr(out), _ptr(mag))
     if rc:
         raise ValueError("q8o_qdot_f64_at failed: %d" % rc)
+    return out, mag
+
+
+def _check_scales_t(A, AS, W, WST):
+    M, K = A.shape
+    N = W.shape[0]
+    AS = _c(AS, np.float32)
+    WST = _c(WST, np.float32)
+    if AS.shape != (M, K // BLOCK) or WST.shape != (K // BLOCK, N):
+        raise ValueError("scales must be AS [M, K/32] and WST [K/32, N]")
+    return AS, WST
+
+
+def qmma_f64(A, AS, W, WST):
+    """The ``qmma_t`` definition in f64 (weight scales ``WST [K/32, N]``): ``(out, abs_terms)``."""
+    A, W = _check_ops(A, W)
+    AS, WST = _check_scales_t(A, AS, W, WST)
+    M, K = A.shape
+    N = W.shape[0]
+    out = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64)
+    rc = _load().q8o_qmma_f64(_ptr(A), _ptr(AS), _ptr(W), _ptr(WST), M, N, K,
+                             _ptr(out), _ptr(mag))
+    if rc:
+        raise ValueError("q8o_qmma_f64 failed: %d" % rc)
+    return out, mag
+
+
+def qmma_f64_at(A, AS, W, WST, ii, jj):
+    """``qmma_t`` at sampled positions ``(ii[s], jj[s])``: ``(out [S], abs_terms [S])``."""
+    A, W = _check_ops(A, W)
+    AS, WST = _check_scales_t(A, AS, W, WST)
+    M, K = A.shape
+    N = W.shape[0]
+    ii = _c(ii, np.int64)
+    jj = _c(jj, np.int64)
+    if ii.shape != jj.shape or ii.ndim != 1:
+        raise ValueError("ii and jj must be 1-D and equal length")
+    out = np.empty(ii.shape[0], np.float64)
+    mag = np.empty(ii.shape[0], np.float64)
+    rc = _load().q8o_qmma_f64_at(_ptr(A), _ptr(AS), _ptr(W), _ptr(WST), M, N, K,
+                                _ptr(ii), _ptr(jj), ii.shape[0], _ptr(out), _ptr(mag))
+    if rc:
+        raise ValueError("q8o_qmma_f64_at failed: %d" % rc)
     return out, mag
 
 

@@ -10,7 +10,10 @@ Two formulations of the Q8_0 contraction in exact rational arithmetic
   formulation the "Quantized built-ins and formats" page mentions under Q8_0
   (bytes converted to float, scale applied per block).
 
-By distributivity the two are equal as rationals; the tests assert that, and
+* ``exact_definition_qmma``: the ``qmma_t`` row of the same table, whose
+  weight scales are stored transposed, ``w_scales[b][j]`` (``[K/32, N]``).
+
+By distributivity the first two are equal as rationals; the tests assert that, and
 that the f64 oracle lies within its rounding bound of them.  Pure Python
 loops: only for tiny M, N, K.
 """
@@ -80,6 +83,26 @@ def exact_abs_terms(A, AS, W, WS):
             for b in range(KB):
                 p = sum(int(A[i, b * BLOCK + t]) * int(W[j, b * BLOCK + t]) for t in range(BLOCK))
                 total += abs(Fraction(float(AS[i, b])) * Fraction(float(WS[j, b])) * p)
+            row.append(total)
+        out.append(row)
+    return out
+
+
+def exact_definition_qmma(A, AS, W, WST):
+    """``[[Fraction]]``: sum_b AS[i,b]*WST[b,j]*sum_{k in b} A[i,k]*W[j,k] (``WST [K/32, N]``)."""
+    A = np.asarray(A)
+    W = np.asarray(W)
+    M, K = A.shape
+    N = W.shape[0]
+    KB = K // BLOCK
+    out = []
+    for i in range(M):
+        row = []
+        for j in range(N):
+            total = Fraction(0)
+            for b in range(KB):
+                p = sum(int(A[i, b * BLOCK + t]) * int(W[j, b * BLOCK + t]) for t in range(BLOCK))
+                total += Fraction(float(AS[i, b])) * Fraction(float(WST[b, j])) * p
             row.append(total)
         out.append(row)
     return out

@@ -12,6 +12,8 @@
  *     row qdot_t: out[i,j] = sum over 32-wide blocks b of
  *     a_scales[i,b] * w_scales[j,b] * (sum over k in b of a[i,k] * w[j,k]);
  *     scales are [M, K/32] and [N, K/32].
+ *   - the same table, row qmma_t: the same sum, with w_scales stored
+ *     transposed, [K/32, N] (w_scales[b][j]).
  *   - "Quantized built-ins and formats", section "Q8_0": signed bytes with
  *     one scale per block of 32 values; activations are quantized the same
  *     way; the inner sum is taken in integers (four bytes at a time with
@@ -172,5 +174,51 @@ int q8o_block_partials_at(const int8_t *A, const int8_t *W, int64_t M, int64_t N
         for (int64_t b = 0; b < KB; ++b)
             P[s * KB + b] = block_dot(A + ii[s] * K + b * Q8_BLOCK,
                                       W + jj[s] * K + b * Q8_BLOCK);
+    return 0;
+}
+
+/* One output of the qmma_t form: weight scales WST[b][j], f32 [K/32][N]. */
+static void qmma_one(const int8_t *A, const float *AS, const int8_t *W,
+                     const float *WST, int64_t i, int64_t j, int64_t N, int64_t K,
+                     double *out, double *abs_terms) {
+    const int64_t KB = K / Q8_BLOCK;
+    double acc = 0.0, mag = 0.0;
+    for (int64_t b = 0; b < KB; ++b) {
+        int32_t p = block_dot(A + i * K + b * Q8_BLOCK, W + j * K + b * Q8_BLOCK);
+        double s = (double)AS[i * KB + b] * (double)WST[b * N + j]; /* exact */
+        double term = s * (double)p;
+        acc += term;
+        mag += fabs(term);
+    }
+    *out = acc;
+    *abs_terms = mag;
+}
+
+/*
+ * qmma_t in f64: out[i][j] = sum_b AS[i,b] * WST[b,j] * P[i,j,b], in block
+ * order, and abs_terms as for q8o_qdot_f64.  WST f32 [K/32][N].
+ */
+int q8o_qmma_f64(const int8_t *A, const float *AS, const int8_t *W,
+                 const float *WST, int64_t M, int64_t N, int64_t K,
+                 double *out, double *abs_terms) {
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            qmma_one(A, AS, W, WST, i, j, N, K, out + i * N + j, abs_terms + i * N + j);
+    return 0;
+}
+
+/* qmma_t at `count` sampled output positions (ii[s], jj[s]). */
+int q8o_qmma_f64_at(const int8_t *A, const float *AS, const int8_t *W,
+                    const float *WST, int64_t M, int64_t N, int64_t K,
+                    const int64_t *ii, const int64_t *jj, int64_t count,
+                    double *out, double *abs_terms) {
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0 || count < 0) return -1;
+    for (int64_t s = 0; s < count; ++s)
+        if (ii[s] < 0 || ii[s] >= M || jj[s] < 0 || jj[s] >= N) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < count; ++s)
+        qmma_one(A, AS, W, WST, ii[s], jj[s], N, K, out + s, abs_terms + s);
     return 0;
 }

@@ -30,6 +30,7 @@ MUTANTS = {
     "ties_away_from_zero": ("rintf(xb[t] / scale)", "roundf(xb[t] / scale)"),
     "scale_over_128": ("amax / 127.0f", "amax / 128.0f"),
     "reciprocal_multiply": ("rintf(xb[t] / scale)", "rintf(xb[t] * (1.0f / scale))"),
+    "qmma_scale_not_transposed": ("(double)WST[b * N + j]", "(double)WST[j * KB + b]"),
     "transposed_weight_operand": ("W + j * K + b * Q8_BLOCK);\n        double s",
                                   "W + (j % 1) * K + b * Q8_BLOCK);\n        double s"),
 }

@@ -67,6 +67,37 @@ def test_exact_rational_bruteforce(M, N, K, seed):
             assert abs(mag[i, j] - float(ex_abs[i][j])) <= bound
 
 
+@pytest.mark.parametrize("M,N,K,seed", [(2, 3, 64, 11), (3, 5, 128, 12), (1, 2, 96, 13)])
+def test_qmma_exact_rational_bruteforce(M, N, K, seed):
+    """qmma_t (weight scales [K/32, N]) against exact rationals; N != K/32 so a
+    transposed index reads a different scale."""
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 100)
+    AS = synth.random_scales((M, K // 32), seed + 200, 1e-4, 10.0)
+    WST = synth.random_scales((K // 32, N), seed + 300, 1e-4, 10.0)
+    ex = brute.exact_definition_qmma(A, AS, W, WST)
+    out, mag = oracle.qmma_f64(A, AS, W, WST)
+    KB = K // 32
+    for i in range(M):
+        for j in range(N):
+            bound = 2.0 * KB * 2.0 ** -53 * float(mag[i, j]) + 1e-300
+            assert abs(out[i, j] - float(ex[i][j])) <= bound
+    o2, m2 = oracle.qmma_f64_at(A, AS, W, WST, np.repeat(np.arange(M), N), np.tile(np.arange(N), M))
+    assert np.array_equal(o2, out.ravel()) and np.array_equal(m2, mag.ravel())
+
+
+def test_qmma_is_qdot_with_transposed_scales():
+    """Storing the weight scales transposed changes nothing else: same terms in
+    the same block order, so the f64 results agree bit for bit."""
+    A = synth.random_i8((5, 320), 21)
+    W = synth.random_i8((7, 320), 22)
+    AS = synth.random_scales((5, 10), 23, 1e-3, 1.0)
+    WS = synth.random_scales((7, 10), 24, 1e-3, 1.0)
+    o1, m1 = oracle.qdot_f64(A, AS, W, WS)
+    o2, m2 = oracle.qmma_f64(A, AS, W, np.ascontiguousarray(WS.T))
+    assert np.array_equal(o1, o2) and np.array_equal(m1, m2)
+
+
 def test_partials_match_numpy_int64_and_bound():
     M, N, K = 5, 7, 320
     A = synth.random_i8((M, K), 11)
