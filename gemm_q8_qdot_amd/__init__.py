@@ -28,7 +28,7 @@ Q8_ERANGE = -4
 Q8_ELAUNCH = -5
 
 # Every symbol include/q8qdot.h declares.
-EXPORTS = ("q8_qdot", "q8_qdot_stream", "q8_qdot_partials", "q8_qdot_path",
+EXPORTS = ("q8_qdot", "q8_qdot_stream", "q8_qmma", "q8_qdot_partials", "q8_qdot_path",
            "q8_quantize", "q8_strerror", "q8_version")
 
 _lock = threading.Lock()
@@ -62,6 +62,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.q8_qdot.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci]
         lib.q8_qdot_stream.restype = ci
         lib.q8_qdot_stream.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
+        lib.q8_qmma.restype = ci
+        lib.q8_qmma.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qdot_partials.restype = ci
         lib.q8_qdot_partials.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qdot_path.restype = ci
@@ -103,6 +105,12 @@ def q8_qdot_raw(A: int, AS: int, W: int, WS: int, C: int, M: int, N: int, K: int
                 stream: int = 0) -> int:
     """``q8_qdot_stream`` on raw device addresses; returns the status."""
     return load().q8_qdot_stream(A, AS, W, WS, C, M, N, K, stream or None)
+
+
+def q8_qmma_raw(A: int, AS: int, W: int, WST: int, C: int, M: int, N: int, K: int,
+                stream: int = 0) -> int:
+    """``q8_qmma`` (weight scales ``[K/32, N]``) on raw device addresses; returns the status."""
+    return load().q8_qmma(A, AS, W, WST, C, M, N, K, stream or None)
 
 
 def q8_qdot_partials_raw(A: int, W: int, P: int, M: int, N: int, K: int, stream: int = 0) -> int:
@@ -168,6 +176,26 @@ def q8_qdot(A, AS, W, WS, C=None, stream=None):
 
 
 q8_qdot_stream = q8_qdot
+
+
+def q8_qmma(A, AS, W, WST, C=None, stream=None):
+    """``C[M, N] = qmma_t(A, AS, W, WST)``: as :func:`q8_qdot` with the weight
+    scales stored transposed, ``WST`` f32 ``[K/32, N]``."""
+    torch = _torch()
+    M, K = A.shape
+    N = W.shape[0]
+    KB = K // 32
+    _need(A, torch.int8, (M, K), "A")
+    _need(AS, torch.float32, (M, KB), "AS")
+    _need(W, torch.int8, (N, K), "W")
+    _need(WST, torch.float32, (KB, N), "WST")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _need(C, torch.float32, (M, N), "C")
+    s = stream.cuda_stream if stream is not None else _current_stream(A.device)
+    st = load().q8_qmma(_ptr(A), _ptr(AS), _ptr(W), _ptr(WST), _ptr(C), M, N, K, s or None)
+    _check(st, "q8_qmma")
+    return C
 
 
 def q8_qdot_partials(A, W, P=None, stream=None):

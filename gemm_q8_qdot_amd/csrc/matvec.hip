@@ -52,7 +52,8 @@ constexpr int kMatvecMaxWaves = Q8_MV_MAX_WAVES;
 constexpr int kMatvecMaxWavesLong = Q8_MV_MAX_WAVES_LONG;
 constexpr int kLoadsInFlight = Q8_MV_LOADS;  // 16-byte weight loads per lane per row group
 
-template <int S, int R, bool PARTIALS>
+// WST: weight scales stored transposed, [K/32][N] (the qmma_t form).
+template <int S, int R, bool PARTIALS, bool WST>
 __global__ void __launch_bounds__(kMatvecThreads)
 matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
               const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -83,7 +84,20 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     };
     if (nchunks == 1) load_a(0);
 
-    for (int g = wave; g < groups; g += nwaves) {
+    // Transposed weight scales: a workgroup's rows are consecutive in each
+    // pass, so their scales of one block are consecutive in WS; the
+    // workgroup stages them for the chunk in LDS ([block][row]) instead of
+    // each lane gathering one scale per row (32 rows per load instruction).
+    constexpr int kRowsWG = (kMatvecThreads / kWave) * R;
+    __shared__ float ws_stage[WST ? S * (kStepBytes / kBlock) * kRowsWG : 1];
+
+    // Every wave of a workgroup runs the same passes (the staging above
+    // synchronizes the workgroup); a wave past the last row group computes
+    // on masked (zero) rows and stores nothing.
+    const int wg_passes = (groups + nwaves - 1) / nwaves;
+    for (int pass = 0; pass < wg_passes; ++pass) {
+        const int g = wave + pass * nwaves;
+        if (!WST && g >= groups) break;
         const int j0 = g * R;
         float acc[R];
 #pragma unroll
@@ -91,6 +105,23 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 
         for (int c = 0; c < nchunks; ++c) {
             if (nchunks > 1) load_a(c);
+            // Transposed scales of this pass's rows for the chunk, loaded first
+            // (consecutive threads read consecutive rows of one block).
+            constexpr int kChunkBlocks = S * (kStepBytes / kBlock);
+            constexpr int kStageN = kChunkBlocks * kRowsWG;
+            constexpr int kStagePer = (kStageN + kMatvecThreads - 1) / kMatvecThreads;
+            float wst_reg[WST ? kStagePer : 1];
+            if constexpr (!PARTIALS && WST) {
+                const int kb0 = c * kChunkBlocks;
+                const int jw0 = (blockIdx.x * (kMatvecThreads / kWave) + pass * nwaves) * R;
+#pragma unroll
+                for (int t = 0; t < kStagePer; ++t) {
+                    const int idx = threadIdx.x + t * kMatvecThreads;
+                    const int kb = kb0 + idx / kRowsWG;
+                    const int j = jw0 + idx % kRowsWG;
+                    wst_reg[t] = (idx < kStageN && kb < KB && j < N) ? WS[(int64_t)kb * N + j] : 0.0f;
+                }
+            }
             v4i w[R][S];
             float ws[R][S];
             // Issue every load of the row group before the first use.
@@ -105,9 +136,28 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const bool ok = row_ok && off < K;
                     w[r][s] = ok ? (Q8_MV_NT ? load16_stream(Wj + off) : load16(Wj + off))
                                  : v4i{0, 0, 0, 0};
-                    if constexpr (!PARTIALS)
+                    if constexpr (!PARTIALS && !WST)
                         ws[r][s] = ok ? WS[(int64_t)j * KB + off / kBlock] : 0.0f;
                 }
+            }
+            if constexpr (!PARTIALS && WST) {
+                // Barriers without a memory-wait on the weight loads in flight:
+                // only this wave's LDS accesses must be complete.
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // chunk c-1 read
+#pragma unroll
+                for (int t = 0; t < kStagePer; ++t) {
+                    const int idx = threadIdx.x + t * kMatvecThreads;
+                    if (idx < kStageN) ws_stage[idx] = wst_reg[t];
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                const int wrow = (threadIdx.x / kWave) * R;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        const int kbl = (s * kStepBytes + lane * 16) / kBlock;  // block within the chunk
+                        ws[r][s] = ws_stage[kbl * kRowsWG + wrow + r];
+                    }
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -136,32 +186,41 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     }
 }
 
-template <int S, bool PARTIALS>
+template <int S, bool PARTIALS, bool WST>
 hipError_t launch_s(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                     float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     // Rows per wave: at least kLoadsInFlight 16-byte weight loads per lane
     // per row group (more rows only for short rows).  Measured on MI355X:
     // many light waves beat few heavy ones; long rows (K >= 8 KiB, large
     // VGPR footprint) prefer a grid that fits the chip at once.
-    constexpr int R0 = kLoadsInFlight / S;
+    // With transposed weight scales, more rows per wave make the workgroup's
+    // rows of one block's scales span whole cache lines (16 rows = 64 bytes).
+    constexpr int R0w = kLoadsInFlight / S;
+    // (launch_any caps S at 8 for them, so R = 2 stays within the VGPRs.)
+    constexpr int R0 = WST ? (S <= 4 ? (R0w > 4 ? R0w : 4) : (R0w > 2 ? R0w : 2)) : R0w;
     constexpr int R = R0 >= 8 ? 8 : (R0 >= 4 ? 4 : (R0 >= 2 ? 2 : 1));
     constexpr int max_waves = S >= 8 ? kMatvecMaxWavesLong : kMatvecMaxWaves;
-    const int groups = (N + R - 1) / R;
-    const int waves = groups < max_waves ? groups : max_waves;
-    const int wgs = (waves + kMatvecThreads / kWave - 1) / (kMatvecThreads / kWave);
-    dim3 grid(wgs, M);
-    matvec_kernel<S, R, PARTIALS><<<grid, kMatvecThreads, 0, stream>>>(A, AS, W, WS, C, P, N, K);
-    return hipGetLastError();
+    if constexpr (WST && S > 8) {
+        return hipErrorInvalidValue;  // never dispatched (steps capped at 8)
+    } else {
+        const int groups = (N + R - 1) / R;
+        const int waves = groups < max_waves ? groups : max_waves;
+        const int wgs = (waves + kMatvecThreads / kWave - 1) / (kMatvecThreads / kWave);
+        dim3 grid(wgs, M);
+        matvec_kernel<S, R, PARTIALS, WST><<<grid, kMatvecThreads, 0, stream>>>(A, AS, W, WS, C, P, N, K);
+        return hipGetLastError();
+    }
 }
 
-template <bool PARTIALS>
+template <bool PARTIALS, bool WST>
 hipError_t launch_any(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                       float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     int steps = (K + kStepBytes - 1) / kStepBytes;
     if (steps > kMaxSteps) steps = kMaxSteps;
+    if (WST && steps > 8) steps = 8;  // longer rows in chunks of 8 KiB
     switch (steps) {
 #define Q8_MATVEC_CASE(S_) \
-    case S_: return launch_s<S_, PARTIALS>(A, AS, W, WS, C, P, M, N, K, stream);
+    case S_: return launch_s<S_, PARTIALS, WST>(A, AS, W, WS, C, P, M, N, K, stream);
         Q8_MATVEC_CASE(1) Q8_MATVEC_CASE(2) Q8_MATVEC_CASE(3) Q8_MATVEC_CASE(4)
         Q8_MATVEC_CASE(5) Q8_MATVEC_CASE(6) Q8_MATVEC_CASE(7) Q8_MATVEC_CASE(8)
         Q8_MATVEC_CASE(9) Q8_MATVEC_CASE(10) Q8_MATVEC_CASE(11) Q8_MATVEC_CASE(12)
@@ -174,9 +233,10 @@ hipError_t launch_any(const int8_t* A, const float* AS, const int8_t* W, const f
 }  // namespace
 
 hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    if (P != nullptr) return launch_any<true>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_any<false>(A, AS, W, WS, C, P, M, N, K, stream);
+                         float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
+    if (P != nullptr) return launch_any<true, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_any<false, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_any<false, false>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 }  // namespace q8

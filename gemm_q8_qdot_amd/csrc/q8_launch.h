@@ -11,8 +11,9 @@ namespace q8 {
 
 // M < 8: wave64 matvec, one activation row per grid row (blockIdx.y).
 // P == nullptr -> f32 output C; otherwise int32 partials P, C unused.
+// ws_t: WS is stored transposed, [K/32][N] (the qmma_t form); else [N][K/32].
 hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream);
+                         float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream);
 
 // M >= 8: int8-MFMA block GEMM.  Same P convention.
 // qgemm_variant: 1 = one workgroup per 32 x 32 tile with the contraction
@@ -20,9 +21,10 @@ hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, cons
 // tiles (large M and N).
 int qgemm_variant(int M, int N, int K);
 hipError_t launch_qgemm(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream);
+                        float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream);
 hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                               float* C, int32_t* P, int M, int N, int K, hipStream_t stream);
+                               float* C, int32_t* P, int M, int N, int K, bool ws_t,
+                               hipStream_t stream);
 
 // Q8_0 quantization of f32 rows.
 hipError_t launch_quantize(const float* X, int8_t* Q, float* D, int rows, int K,

@@ -32,8 +32,9 @@ int check_range(int64_t M, int64_t N, int64_t K, bool partials) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ELAUNCH; }
 
+// ws_t: WS is the qmma_t form, stored transposed [K/32][N].
 int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS, float* C,
-             int32_t* P, int M, int N, int K, hipStream_t stream) {
+             int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
     int st = check_shape(M, N, K);
     if (st != Q8_OK) return st;
     st = check_range(M, N, K, P != nullptr);
@@ -47,8 +48,10 @@ int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
         if (!aligned(C, 4)) return Q8_EALIGN;
         return status_of(q8::launch_fill_zero(C, (int64_t)M * N, stream));
     }
-    // The block GEMMs address a 32-row operand tile with 32-bit offsets.
+    // The block GEMMs address a 32-row operand tile, and the transposed
+    // weight scales from a column to the end, with 32-bit offsets.
     if (M > kMatvecMaxM && (int64_t)K * 32 > INT32_MAX) return Q8_ERANGE;
+    if (M > kMatvecMaxM && ws_t && (int64_t)(K / 32) * N * 4 > INT32_MAX) return Q8_ERANGE;
     if (A == nullptr || W == nullptr) return Q8_ENULL;
     if (!partials && (AS == nullptr || WS == nullptr || C == nullptr)) return Q8_ENULL;
     if (!aligned(A, 16) || !aligned(W, 16)) return Q8_EALIGN;
@@ -58,8 +61,8 @@ int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
         return Q8_EALIGN;
     }
     hipError_t e = M <= kMatvecMaxM
-                       ? q8::launch_matvec(A, AS, W, WS, C, P, M, N, K, stream)
-                       : q8::launch_qgemm(A, AS, W, WS, C, P, M, N, K, stream);
+                       ? q8::launch_matvec(A, AS, W, WS, C, P, M, N, K, ws_t, stream)
+                       : q8::launch_qgemm(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
     return status_of(e);
 }
 
@@ -67,12 +70,17 @@ int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
 
 Q8_API int q8_qdot_stream(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                           float* C, int M, int N, int K, void* stream) {
-    return run_qdot(A, AS, W, WS, C, nullptr, M, N, K, static_cast<hipStream_t>(stream));
+    return run_qdot(A, AS, W, WS, C, nullptr, M, N, K, false, static_cast<hipStream_t>(stream));
+}
+
+Q8_API int q8_qmma(const int8_t* A, const float* AS, const int8_t* W, const float* WST,
+                   float* C, int M, int N, int K, void* stream) {
+    return run_qdot(A, AS, W, WST, C, nullptr, M, N, K, true, static_cast<hipStream_t>(stream));
 }
 
 Q8_API int q8_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                    float* C, int M, int N, int K) {
-    return run_qdot(A, AS, W, WS, C, nullptr, M, N, K, nullptr);
+    return run_qdot(A, AS, W, WS, C, nullptr, M, N, K, false, nullptr);
 }
 
 Q8_API int q8_qdot_partials(const int8_t* A, const int8_t* W, int32_t* P, int M, int N, int K,
@@ -83,7 +91,7 @@ Q8_API int q8_qdot_partials(const int8_t* A, const int8_t* W, int32_t* P, int M,
         if (M == 0 || N == 0 || K == 0) return Q8_OK;
         return Q8_ENULL;
     }
-    return run_qdot(A, nullptr, W, nullptr, nullptr, P, M, N, K, static_cast<hipStream_t>(stream));
+    return run_qdot(A, nullptr, W, nullptr, nullptr, P, M, N, K, false, static_cast<hipStream_t>(stream));
 }
 
 Q8_API int q8_qdot_path(int M, int N, int K) {

@@ -110,10 +110,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(const lds_char*)p);
 }
 
-// WSX4: K/32 is a multiple of the stage's 4 blocks, so every stage is whole
-// and each weight-scale row's 4 block scales come as one 16-byte load
-// (LDS layout [row][block]); otherwise one dword per (block, row) with
-// blocks past K read as 0 (layout [block][row]).
+// Weight-scale modes (WSM):
+//   0  WS [N][K/32], one dword per (block, row); LDS [block][row]
+//   1  WS [N][K/32] with K/32 a multiple of the stage's 4 blocks (whole
+//      stages): a row's 4 block scales as one 16-byte load; LDS [row][block]
+//   2  WS stored transposed [K/32][N] (the qmma_t form), one dword per
+//      (block, row); LDS [block][row]
+//   3  transposed, whole stages, N % 4 == 0: 16 bytes = 4 rows of one block
+//      per lane; LDS [block][row]
+// Blocks past K (a partial last stage, modes 0 and 2) read as 0.
 //
 // Wave roles: wave wv runs on SIMD wv % 4 (waves are placed round-robin)
 // and computes the 32 activation rows 32 (wv % 4) .. against tiles
@@ -121,7 +126,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // every block: four waves per SIMD keep the VALU epilogue of one wave going
 // while another waits on its MFMA or LDS reads, and every output tile has a
 // single owner (no cross-wave reduction).
-template <int TN, bool PARTIALS, bool WSX4>
+template <int TN, bool PARTIALS, int WSM>
 __global__ void __launch_bounds__(kStagedThreads, 1)
 qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -137,17 +142,22 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     //   slot 1: W rows 8 wv ..
     //   slot 2: W rows 8 (16 + wv) .. for wv < 12; activation-scale job
     //           2 (wv - 12) for wv >= 12
-    //   slot 3: WSX4: weight-scale job wv for wv < 4, activation-scale job
-    //           2 (wv - 12) + 1 for wv >= 12;  else activation-scale job
-    //           2 (wv - 12) + 1 for wv >= 12, then weight-scale job wv
+    //   slot 3: 16-byte weight-scale modes: weight-scale job wv for wv < 4,
+    //           activation-scale job 2 (wv - 12) + 1 for wv >= 12;  dword
+    //           modes: activation-scale job 2 (wv - 12) + 1 for wv >= 12,
+    //           then weight-scale job wv
     // Activation-scale job e: block e / 2, rows 64 (e % 2) + lane (dword).
-    // Weight-scale job e: WSX4: rows 64 e + lane, blocks 0..3 (16 bytes);
-    // else block e / 4, rows 64 (e % 4) + lane (dword).
+    // Weight-scale job e: mode 1: rows 64 e + lane, blocks 0..3; mode 3:
+    // block e, rows 4 lane .. 4 lane + 3; modes 0, 2: block e / 4, rows
+    // 64 (e % 4) + lane (dword).
     constexpr int kWJobs = BN / kRowsPerLoad;             // 28 for TN = 7
     static_assert(kBM / kRowsPerLoad == kStagedWaves, "one A job per wave");
     static_assert(kWJobs == kStagedWaves + 12, "W jobs: two for waves 0-11, one for 12-15");
     static_assert(kSB * kBM / kWave == 8, "eight activation-scale jobs");
     static_assert(kWSRows * 16 / 1024 == 4 && kSB * kWSRows / kWave == kStagedWaves, "weight-scale jobs");
+    constexpr bool WSX4 = WSM == 1 || WSM == 3;   // 16-byte weight-scale jobs, whole stages
+    constexpr bool WST = WSM >= 2;                // weight scales stored [K/32][N]
+    constexpr bool WS_ROWMAJOR = WSM == 1;        // LDS [row][block] (else [block][row])
     constexpr int kLoadsPerWave = WSX4 ? 4 : 5;  // loads per wave per stage (all waves)
     extern __shared__ __align__(16) unsigned char smem_raw[];
     StagedStage<TN>* ring = reinterpret_cast<StagedStage<TN>*>(smem_raw);
@@ -180,7 +190,10 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const v4i dA = make_desc(A + (int64_t)i0 * K, (int64_t)rows_a * K);
     const v4i dW = make_desc(W + (int64_t)j0 * K, (int64_t)rows_w * K);
     const v4i dAS = make_desc(PARTIALS ? nullptr : AS + (int64_t)i0 * KB, (int64_t)rows_a * KB * 4);
-    const v4i dWS = make_desc(PARTIALS ? nullptr : WS + (int64_t)j0 * KB, (int64_t)rows_w * KB * 4);
+    // Transposed weight scales: from column j0 to the end of the array
+    // (columns past the tile meet zero weight rows and are never stored).
+    const v4i dWS = make_desc(PARTIALS ? nullptr : WS + (WST ? (int64_t)j0 : (int64_t)j0 * KB),
+                              WST ? ((int64_t)KB * N - j0) * 4 : (int64_t)rows_w * KB * 4);
 
     // A/W job of rows 8 q' .. 8 q' + 7: lane fills physical chunk lane % 8 of
     // row 8 q' + lane / 8, i.e. reads logical chunk
@@ -232,9 +245,18 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         StagedStage<TN>& sg = ring[rs];
         const int kb0 = st * kSB;
         const bool to_slot = real && !PARTIALS;
-        if constexpr (WSX4) {  // whole stages: every block is inside K
+        if constexpr (WSM == 1) {  // whole stages: every block is inside K
             const int vo = to_slot ? voff_scale + e * kWave * KB * 4 : kNoRead;
             dma16(dWS, lds_addr(to_slot ? (const void*)&sg.ws[e * kWave * kSB] : (const void*)spare), vo, kb0 * 4);
+        } else if constexpr (WSM == 3) {  // block e of the stage, 4 rows per lane
+            const int vo = to_slot ? ((kb0 + e) * N + 4 * lane) * 4 : kNoRead;
+            dma16(dWS, lds_addr(to_slot ? (const void*)&sg.ws[e * kWSRows] : (const void*)spare), vo, 0);
+        } else if constexpr (WSM == 2) {  // block e / 4, rows 64 (e % 4) + lane
+            const int sblk = e / 4, h = e % 4;
+            const bool ok = to_slot && sblk < KB - kb0;
+            const int vo = ok ? ((kb0 + sblk) * N + h * kWave + lane) * 4 : kNoRead;
+            dma4(dWS, lds_addr(to_slot ? (const void*)&sg.ws[sblk * kWSRows + h * kWave] : (const void*)spare),
+                 vo, 0);
         } else {
             const int sblk = e / 4, h = e % 4;
             const bool ok = to_slot && sblk < KB - kb0;
@@ -324,7 +346,7 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                 const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
                 // the (ws_hi, bias product) pair of this lane's weight row
                 const int wrow = (t0 + t) * kTile + col;
-                const float2 wp = ws_pair(WSX4 ? sg.ws[wrow * kSB + s] : sg.ws[s * kWSRows + wrow]);
+                const float2 wp = ws_pair(WS_ROWMAJOR ? sg.ws[wrow * kSB + s] : sg.ws[s * kWSRows + wrow]);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
@@ -394,7 +416,7 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     else run(std::integral_constant<int, 1>());
 }
 
-template <int TN, bool PARTIALS, bool WSX4>
+template <int TN, bool PARTIALS, int WSM>
 hipError_t launch_staged_v(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                            float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     constexpr int BN = TN * kTile;
@@ -407,7 +429,7 @@ hipError_t launch_staged_v(const int8_t* A, const float* AS, const int8_t* W, co
     constexpr size_t need = staged_smem_bytes<TN>();
     constexpr size_t smem = need > 82 * 1024 ? need : 82 * 1024;
     static_assert(smem <= 160 * 1024, "LDS budget");
-    auto kern = qgemm_staged_kernel<TN, PARTIALS, WSX4>;
+    auto kern = qgemm_staged_kernel<TN, PARTIALS, WSM>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -422,11 +444,19 @@ hipError_t launch_staged_v(const int8_t* A, const float* AS, const int8_t* W, co
 
 template <int TN, bool PARTIALS>
 hipError_t launch_staged(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    // 16-byte weight-scale loads need whole stages and a 16-byte aligned WS.
-    if ((K / kBlock) % kSB == 0 && (reinterpret_cast<uintptr_t>(WS) & 15) == 0)
-        return launch_staged_v<TN, PARTIALS, true>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_staged_v<TN, PARTIALS, false>(A, AS, W, WS, C, P, M, N, K, stream);
+                         float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
+    // 16-byte weight-scale loads need whole stages and a 16-byte aligned WS
+    // (and, transposed, rows of 4-aligned length).
+    const bool whole = (K / kBlock) % kSB == 0 && (reinterpret_cast<uintptr_t>(WS) & 15) == 0;
+    if constexpr (PARTIALS) {
+        return launch_staged_v<TN, PARTIALS, 0>(A, AS, W, WS, C, P, M, N, K, stream);
+    } else if (ws_t) {
+        if (whole && N % 4 == 0) return launch_staged_v<TN, PARTIALS, 3>(A, AS, W, WS, C, P, M, N, K, stream);
+        return launch_staged_v<TN, PARTIALS, 2>(A, AS, W, WS, C, P, M, N, K, stream);
+    } else {
+        if (whole) return launch_staged_v<TN, PARTIALS, 1>(A, AS, W, WS, C, P, M, N, K, stream);
+        return launch_staged_v<TN, PARTIALS, 0>(A, AS, W, WS, C, P, M, N, K, stream);
+    }
 }
 
 constexpr int kStagedTN = 7;  // 128 x 224 tiles: 512 x 14336 is exactly 256 of them
@@ -443,12 +473,12 @@ int qgemm_variant(int M, int N, int K) {
 }
 
 hipError_t launch_qgemm(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+                        float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
     if (qgemm_variant(M, N, K) == 2) {
-        if (P != nullptr) return launch_staged<kStagedTN, true>(A, AS, W, WS, C, P, M, N, K, stream);
-        return launch_staged<kStagedTN, false>(A, AS, W, WS, C, P, M, N, K, stream);
+        if (P != nullptr) return launch_staged<kStagedTN, true>(A, AS, W, WS, C, P, M, N, K, false, stream);
+        return launch_staged<kStagedTN, false>(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
     }
-    return launch_qgemm_ksplit(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_qgemm_ksplit(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
 }
 
 }  // namespace q8

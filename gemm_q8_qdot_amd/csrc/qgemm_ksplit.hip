@@ -70,7 +70,8 @@ struct KsRaw {
     float as[2], ws[2];
 };
 
-template <int NW, bool PF, bool PARTIALS>
+// WST: weight scales stored transposed, [K/32][N] (the qmma_t form).
+template <int NW, bool PF, bool PARTIALS, bool WST>
 __global__ void __launch_bounds__(NW * kWave)
 qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -101,9 +102,16 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(W + j0 * K, (int64_t)rows_w * K);
     // (the debug entry passes no scales and reads none)
     const __amdgpu_buffer_rsrc_t rAS = buffer_rsrc(PARTIALS ? nullptr : AS + i0 * KB, (int64_t)rows_a * KB * 4);
-    const __amdgpu_buffer_rsrc_t rWS = buffer_rsrc(PARTIALS ? nullptr : WS + j0 * KB, (int64_t)rows_w * KB * 4);
+    // Weight scales [N][K/32]: this tile's rows.  Transposed [K/32][N]: from
+    // column j0 to the end of the array (columns past the tile belong to
+    // other tiles or the next block row; they meet zero weights and are
+    // never stored).
+    const __amdgpu_buffer_rsrc_t rWS =
+        buffer_rsrc(PARTIALS ? nullptr : WS + (WST ? j0 : j0 * KB),
+                    WST ? ((int64_t)KB * N - j0) * 4 : (int64_t)rows_w * KB * 4);
     const int voff_ops = lrow * K + 16 * lch;             // + 8 q K for group q
     const int voff_sc = (srow * KB + sblk) * 4;           // + 16 k KB * 4 for half k
+    const int voff_wst = (sblk * N + srow) * 4;           // + (kb0 N + 16 k) * 4
 
     // ---- MFMA-side lane roles
     const int half = lane / 32;
@@ -124,12 +132,18 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             raw.w[q] = buffer_load16(rW, v, so);
         }
         if constexpr (!PARTIALS) {
-            const int vs = (kb0 + sblk < KB) ? voff_sc : kNoRead;
+            const bool blk_ok = kb0 + sblk < KB;
+            const int vs = blk_ok ? voff_sc : kNoRead;
+            // transposed: the whole offset in the range-checked lane offset
+            const int vt = blk_ok ? voff_wst + kb0 * N * 4 : kNoRead;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int v = vs == kNoRead ? kNoRead : vs + 16 * k * KB * 4;
                 raw.as[k] = buffer_load_f32(rAS, v, kb0 * 4);
-                raw.ws[k] = buffer_load_f32(rWS, v, kb0 * 4);
+                if constexpr (WST)
+                    raw.ws[k] = buffer_load_f32(rWS, vt == kNoRead ? kNoRead : vt + 16 * k * 4, 0);
+                else
+                    raw.ws[k] = buffer_load_f32(rWS, v, kb0 * 4);
             }
         }
     };
@@ -243,7 +257,7 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     }
 }
 
-template <int NW, bool PF, bool PARTIALS>
+template <int NW, bool PF, bool PARTIALS, bool WST>
 hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                      float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     const int64_t m_tiles = (M + kTile - 1) / kTile;
@@ -252,7 +266,7 @@ hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const fl
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     constexpr size_t smem = ksplit_smem_bytes<NW>();
     static_assert(smem <= 160 * 1024, "LDS budget");
-    auto kern = qgemm_ksplit_kernel<NW, PF, PARTIALS>;
+    auto kern = qgemm_ksplit_kernel<NW, PF, PARTIALS, WST>;
     if (smem > 64 * 1024) {
         static bool attr_set = false;
         if (!attr_set) {
@@ -270,10 +284,12 @@ hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const fl
 }  // namespace
 
 hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                               float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+                               float* C, int32_t* P, int M, int N, int K, bool ws_t,
+                               hipStream_t stream) {
     constexpr bool pf = Q8_KS_PREFETCH != 0;
-    if (P != nullptr) return launch_ks<kKsWaves, pf, true>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_ks<kKsWaves, pf, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (P != nullptr) return launch_ks<kKsWaves, pf, true, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_ks<kKsWaves, pf, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks<kKsWaves, pf, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 }  // namespace q8

@@ -59,7 +59,8 @@ typedef enum {
     Q8_ENULL = -2,   /* a pointer the call must dereference is NULL */
     Q8_EALIGN = -3,  /* A/W/X/Q not 16-byte aligned, or another array not 4-byte aligned */
     Q8_ERANGE = -4,  /* an extent product overflows 64-bit byte addressing, or
-                        M >= 8 with 32 * K > 2^31 - 1 (32-bit tile offsets) */
+                        M >= 8 with 32 * K > 2^31 - 1 (32-bit tile offsets), or
+                        q8_qmma with M >= 8 and (K/32) * N * 4 > 2^31 - 1 */
     Q8_ELAUNCH = -5  /* the HIP runtime rejected the launch (hipGetLastError) */
 } q8_status;
 
@@ -73,6 +74,24 @@ int q8_qdot(const int8_t *A, const float *AS, const int8_t *W, const float *WS,
 /* The same on an explicit HIP stream (hipStream_t passed as void*). */
 int q8_qdot_stream(const int8_t *A, const float *AS, const int8_t *W, const float *WS,
                    float *C, int M, int N, int K, void *stream);
+
+/*
+ * C = qmma_t(A, AS, W, WST): the same sum with the weight scales stored
+ * transposed ("Phobos Language Spec", section "Quantized built-ins", Q8_0
+ * table, row qmma_t; "Quantized built-ins and formats", section "Q8_0"):
+ *
+ *     C[i, j] = sum over blocks b of  AS[i, b] * WST[b, j] * P[i, j, b]
+ *
+ *     WST  f32  [K/32][N]   weight block scales, block-major
+ *
+ * Everything else (A, AS, W, C, conventions, errors) as for q8_qdot_stream.
+ * The pages ask for M and N multiples of 8 here; this library accepts any
+ * M, N >= 0.  For M >= 8, (K/32) * N * 4 must be below 2^31 (32-bit offsets
+ * into WST), else Q8_ERANGE.  The int32 partials do not involve the scales:
+ * q8_qdot_partials serves both forms.
+ */
+int q8_qmma(const int8_t *A, const float *AS, const int8_t *W, const float *WST,
+            float *C, int M, int N, int K, void *stream);
 
 /*
  * Debug entry: P[i][j][b] = the int32 block sum of the qdot_t definition,

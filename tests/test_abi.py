@@ -64,6 +64,7 @@ def test_bad_shapes_rejected(lib, M, N, K):
     assert q8.q8_qdot_raw(16, 16, 16, 16, 16, M, N, K) == q8.Q8_EINVAL
     assert lib.q8_qdot(16, 16, 16, 16, 16, M, N, K) == q8.Q8_EINVAL
     assert q8.q8_qdot_partials_raw(16, 16, 16, M, N, K) == q8.Q8_EINVAL
+    assert q8.q8_qmma_raw(16, 16, 16, 16, 16, M, N, K) == q8.Q8_EINVAL
 
 
 def test_null_pointers_rejected(lib):
@@ -72,6 +73,8 @@ def test_null_pointers_rejected(lib):
                  (ok, ok, ok, 0, ok), (ok, ok, ok, ok, 0)]:
         assert q8.q8_qdot_raw(*args, 1, 64, 64) == q8.Q8_ENULL
         assert q8.q8_qdot_raw(*args, 64, 64, 64) == q8.Q8_ENULL
+        assert q8.q8_qmma_raw(*args, 1, 64, 64) == q8.Q8_ENULL
+        assert q8.q8_qmma_raw(*args, 64, 64, 64) == q8.Q8_ENULL
     assert q8.q8_qdot_partials_raw(0, ok, ok, 8, 8, 64) == q8.Q8_ENULL
     assert q8.q8_qdot_partials_raw(ok, 0, ok, 8, 8, 64) == q8.Q8_ENULL
     assert q8.q8_qdot_partials_raw(ok, ok, 0, 8, 8, 64) == q8.Q8_ENULL
@@ -90,6 +93,8 @@ def test_misaligned_pointers_rejected(lib):
     # f32 arrays off a 4-byte boundary
     assert q8.q8_qdot_raw(base, base + 2, base, base, base, 1, 4, 32) == q8.Q8_EALIGN
     assert q8.q8_qdot_raw(base, base, base, base + 1, base, 1, 4, 32) == q8.Q8_EALIGN
+    assert q8.q8_qmma_raw(base, base, base, base + 2, base, 9, 4, 32) == q8.Q8_EALIGN
+    assert q8.q8_qmma_raw(base + 4, base, base, base, base, 9, 4, 32) == q8.Q8_EALIGN
     assert q8.q8_qdot_raw(base, base, base, base, base + 3, 9, 4, 32) == q8.Q8_EALIGN
     assert q8.q8_qdot_partials_raw(base, base, base + 2, 9, 4, 32) == q8.Q8_EALIGN
     assert q8.q8_qdot_partials_raw(base + 1, base, base, 9, 4, 32) == q8.Q8_EALIGN
@@ -102,6 +107,7 @@ def test_empty_outputs_are_noops(lib):
     # M == 0 or N == 0: nothing launched, pointers not inspected
     assert q8.q8_qdot_raw(0, 0, 0, 0, 0, 0, 5, 64) == q8.Q8_OK
     assert q8.q8_qdot_raw(0, 0, 0, 0, 0, 5, 0, 64) == q8.Q8_OK
+    assert q8.q8_qmma_raw(0, 0, 0, 0, 0, 0, 5, 64) == q8.Q8_OK
     assert q8.q8_qdot_partials_raw(0, 0, 0, 0, 3, 64) == q8.Q8_OK
     assert q8.q8_qdot_partials_raw(0, 0, 0, 3, 3, 0) == q8.Q8_OK
     assert q8.q8_quantize_raw(0, 0, 0, 0, 64) == q8.Q8_OK
@@ -116,6 +122,8 @@ def test_range_overflow_rejected(lib):
     huge_k = 2**26
     assert q8.q8_qdot_raw(16, 16, 16, 16, 16, 8, 4, huge_k) == q8.Q8_ERANGE
     assert q8.q8_qdot_partials_raw(16, 16, 16, 8, 4, huge_k) == q8.Q8_ERANGE
+    # qmma_t with M >= 8 addresses the transposed scales with 32-bit offsets
+    assert q8.q8_qmma_raw(16, 16, 16, 16, 16, 8, 2**20, 2**15) == q8.Q8_ERANGE
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
