@@ -1,4 +1,5 @@
 // Q8_0 matvec for small M (decode step): C[i, :] = qdot_t(A[i, :], AS[i, :], W, WS).
+// (Batches of 2..7 rows with K <= 16 KiB go to matvec_batch.hip.)
 //
 // What is computed: the qdot_t row of the Q8_0 table ("Phobos Language Spec",
 // section "Quantized built-ins"), with the inner block sum in integers as the
@@ -234,6 +235,8 @@ hipError_t launch_any(const int8_t* A, const float* AS, const int8_t* W, const f
 
 hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                          float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
+    if (matvec_batch_fits(M, K))  // several rows: read the weights once for all of them
+        return launch_matvec_batch(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
     if (P != nullptr) return launch_any<true, false>(A, AS, W, WS, C, P, M, N, K, stream);
     if (ws_t) return launch_any<false, true>(A, AS, W, WS, C, P, M, N, K, stream);
     return launch_any<false, false>(A, AS, W, WS, C, P, M, N, K, stream);

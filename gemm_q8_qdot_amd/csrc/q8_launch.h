@@ -15,6 +15,13 @@ namespace q8 {
 hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                          float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream);
 
+// 2 <= M <= 7 with K <= 16 KiB: the activation rows staged in LDS, every
+// weight row read once for all of them.  Same P and ws_t conventions.
+bool matvec_batch_fits(int M, int K);
+hipError_t launch_matvec_batch(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                               float* C, int32_t* P, int M, int N, int K, bool ws_t,
+                               hipStream_t stream);
+
 // M >= 8: int8-MFMA block GEMM.  Same P convention.
 // qgemm_variant: 1 = one workgroup per 32 x 32 tile with the contraction
 // split across its waves (few tiles), 2 = LDS-staged 128 x 224 workgroup

@@ -135,6 +135,21 @@ EDGE = [
 ]
 
 
+# Small decode batches (2..7 activation rows): one weight pass for all rows,
+# at the decode workloads' sizes and at ragged ones.
+BATCH = [(2, 14336, 4096), (4, 4096, 14336), (7, 4096, 4096), (3, 1000, 16384), (5, 333, 1056),
+         (6, 2, 32)]
+
+
+@pytest.mark.parametrize("M,N,K", BATCH)
+def test_small_batch(dev, M, N, K):
+    A = synth.random_i8((M, K), 60 + M)
+    W = synth.random_i8((N, K), 61 + M)
+    AS = synth.random_scales((M, K // 32), 62 + M, 1e-3, 1.0)
+    WS = synth.random_scales((N, K // 32), 63 + M, 1e-3, 1.0)
+    _check_full(A, AS, W, WS, dev, "batch")
+
+
 @pytest.mark.parametrize("M,N,K", EDGE)
 def test_edge_shapes(dev, M, N, K):
     seed = M * 1000003 + N * 101 + K
