@@ -81,6 +81,14 @@ def _load():
             lib.q8o_qmma_f64.argtypes = [p, p, p, p, i64, i64, i64, p, p]
             lib.q8o_qmma_f64_at.restype = ctypes.c_int
             lib.q8o_qmma_f64_at.argtypes = [p, p, p, p, i64, i64, i64, p, p, i64, p, p]
+            lib.q8o_q50_decode.restype = ctypes.c_int
+            lib.q8o_q50_decode.argtypes = [p, p, i64, i64]
+            lib.q8o_q50_block_partials.restype = ctypes.c_int
+            lib.q8o_q50_block_partials.argtypes = [p, p, p, i64, i64, i64]
+            lib.q8o_q50_f64.restype = ctypes.c_int
+            lib.q8o_q50_f64.argtypes = [p, p, p, p, ctypes.c_int, i64, i64, i64, p, p]
+            lib.q8o_q50_f64_at.restype = ctypes.c_int
+            lib.q8o_q50_f64_at.argtypes = [p, p, p, p, ctypes.c_int, i64, i64, i64, p, p, i64, p, p]
             lib.q8o_block_partials_at.restype = ctypes.c_int
             lib.q8o_block_partials_at.argtypes = [p, p, i64, i64, i64, p, p, i64, p]
             _lib = lib
@@ -244,6 +252,92 @@ def block_partials_at(A, W, ii, jj):
     if rc:
         raise ValueError("q8o_block_partials_at failed: %d" % rc)
     return P
+
+
+# ------------------------------------------------------------------ Q5_0
+
+Q50_BLOCK_BYTES = 20
+
+
+def _check_q50(A, W5):
+    A = _c(A, np.int8)
+    W5 = _c(W5, np.uint8)
+    if A.ndim != 2 or W5.ndim != 2 or A.shape[1] % BLOCK:
+        raise ValueError("A [M,K] with K % 32 == 0 and W5 [N, K/32*20]")
+    if W5.shape[1] != A.shape[1] // BLOCK * Q50_BLOCK_BYTES:
+        raise ValueError("W5 must be [N, K/32 * 20] bytes")
+    return A, W5
+
+
+def q50_decode(W5: np.ndarray, K: int) -> np.ndarray:
+    """Q5_0 blocks ``W5 [N, K/32*20]`` (uint8) -> values ``int8 [N, K]`` in ``[-16, 15]``."""
+    W5 = _c(W5, np.uint8)
+    N = W5.shape[0]
+    if K % BLOCK or W5.shape[1] != K // BLOCK * Q50_BLOCK_BYTES:
+        raise ValueError("W5 must be [N, K/32 * 20] bytes")
+    Wd = np.empty((N, K), np.int8)
+    rc = _load().q8o_q50_decode(_ptr(W5), _ptr(Wd), N, K)
+    if rc:
+        raise ValueError("q8o_q50_decode failed: %d" % rc)
+    return Wd
+
+
+def q50_block_partials(A, W5) -> np.ndarray:
+    """Integer block partials against Q5_0 weights: int32 ``[M, N, K/32]``."""
+    A, W5 = _check_q50(A, W5)
+    M, K = A.shape
+    N = W5.shape[0]
+    P = np.empty((M, N, K // BLOCK), np.int32)
+    rc = _load().q8o_q50_block_partials(_ptr(A), _ptr(W5), _ptr(P), M, N, K)
+    if rc:
+        raise ValueError("q8o_q50_block_partials failed: %d" % rc)
+    return P
+
+
+def _q50_f64(A, AS, W5, WS, ws_t):
+    A, W5 = _check_q50(A, W5)
+    M, K = A.shape
+    N = W5.shape[0]
+    AS = _c(AS, np.float32)
+    WS = _c(WS, np.float32)
+    want = (K // BLOCK, N) if ws_t else (N, K // BLOCK)
+    if AS.shape != (M, K // BLOCK) or WS.shape != want:
+        raise ValueError("scales must be AS [M, K/32] and WS %s" % (want,))
+    out = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64)
+    rc = _load().q8o_q50_f64(_ptr(A), _ptr(AS), _ptr(W5), _ptr(WS), int(ws_t), M, N, K,
+                            _ptr(out), _ptr(mag))
+    if rc:
+        raise ValueError("q8o_q50_f64 failed: %d" % rc)
+    return out, mag
+
+
+def q50_qdot_f64(A, AS, W5, WS):
+    """``q50_qdot_t`` in f64 (weight scales ``[N, K/32]``): ``(out, abs_terms)``."""
+    return _q50_f64(A, AS, W5, WS, False)
+
+
+def q50_qmma_f64(A, AS, W5, WST):
+    """``q50_qmma_t`` in f64 (weight scales ``[K/32, N]``): ``(out, abs_terms)``."""
+    return _q50_f64(A, AS, W5, WST, True)
+
+
+def q50_f64_at(A, AS, W5, WS, ws_t, ii, jj):
+    """Q5_0 contraction at sampled positions: ``(out [S], abs_terms [S])``."""
+    A, W5 = _check_q50(A, W5)
+    M, K = A.shape
+    N = W5.shape[0]
+    AS = _c(AS, np.float32)
+    WS = _c(WS, np.float32)
+    ii = _c(ii, np.int64)
+    jj = _c(jj, np.int64)
+    out = np.empty(ii.shape[0], np.float64)
+    mag = np.empty(ii.shape[0], np.float64)
+    rc = _load().q8o_q50_f64_at(_ptr(A), _ptr(AS), _ptr(W5), _ptr(WS), int(ws_t), M, N, K,
+                               _ptr(ii), _ptr(jj), ii.shape[0], _ptr(out), _ptr(mag))
+    if rc:
+        raise ValueError("q8o_q50_f64_at failed: %d" % rc)
+    return out, mag
 
 
 def within_tolerance(C, out64, abs64, rel=1e-5, absol=1e-6):

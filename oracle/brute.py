@@ -106,3 +106,44 @@ def exact_definition_qmma(A, AS, W, WST):
             row.append(total)
         out.append(row)
     return out
+
+
+def q50_values_py(W5_row, K):
+    """Pure-Python Q5_0 decode of one weight row (``K/32 * 20`` bytes) into ``K`` ints.
+
+    Written from the q50 rows of the Q8_0 table ("Phobos Language Spec",
+    "Quantized built-ins"): per 32 values the qh word (little-endian, bit e =
+    bit 4 of element e), then 16 bytes, byte e = element e (low nibble) and
+    element e + 16 (high nibble); value = q - 16.
+    """
+    vals = []
+    for b in range(K // BLOCK):
+        blk = [int(x) for x in W5_row[b * 20:(b + 1) * 20]]
+        qh = blk[0] | (blk[1] << 8) | (blk[2] << 16) | (blk[3] << 24)
+        for e in range(BLOCK):
+            byte = blk[4 + (e % 16)]
+            nib = (byte & 15) if e < 16 else (byte >> 4)
+            vals.append((nib | (((qh >> e) & 1) << 4)) - 16)
+    return vals
+
+
+def exact_definition_q50(A, AS, W5, WS, ws_t=False):
+    """``[[Fraction]]``: the q50 contraction; ``WS`` is ``[N, K/32]`` or, with ``ws_t``, ``[K/32, N]``."""
+    A = np.asarray(A)
+    W5 = np.asarray(W5)
+    M, K = A.shape
+    N = W5.shape[0]
+    KB = K // BLOCK
+    wv = [q50_values_py(W5[j], K) for j in range(N)]
+    out = []
+    for i in range(M):
+        row = []
+        for j in range(N):
+            total = Fraction(0)
+            for b in range(KB):
+                p = sum(int(A[i, b * BLOCK + t]) * wv[j][b * BLOCK + t] for t in range(BLOCK))
+                ws = WS[b, j] if ws_t else WS[j, b]
+                total += Fraction(float(AS[i, b])) * Fraction(float(ws)) * p
+            row.append(total)
+        out.append(row)
+    return out

@@ -14,6 +14,10 @@
  *     scales are [M, K/32] and [N, K/32].
  *   - the same table, row qmma_t: the same sum, with w_scales stored
  *     transposed, [K/32, N] (w_scales[b][j]).
+ *   - the same table, rows q50_qdot_t / q50_qmma_t: the weight is Q5_0
+ *     blocks without their f16 scale, 20 bytes per 32 values: the qh word,
+ *     then 16 bytes, byte e holding element e (low nibble) and element
+ *     e + 16 (high nibble); each element is q - 16.
  *   - "Quantized built-ins and formats", section "Q8_0": signed bytes with
  *     one scale per block of 32 values; activations are quantized the same
  *     way; the inner sum is taken in integers (four bytes at a time with
@@ -220,5 +224,96 @@ int q8o_qmma_f64_at(const int8_t *A, const float *AS, const int8_t *W,
 #pragma omp parallel for schedule(static)
     for (int64_t s = 0; s < count; ++s)
         qmma_one(A, AS, W, WST, ii[s], jj[s], N, K, out + s, abs_terms + s);
+    return 0;
+}
+
+/*
+ * Q5_0 weight blocks (the q50_qdot_t / q50_qmma_t rows of the Q8_0 table).
+ * Block b of weight row j is the 20 bytes at W5 + (j * K/32 + b) * 20: the
+ * qh word (bytes 0..3, little-endian), then bytes 4..19.  Element e < 16 is
+ * the low nibble of byte 4 + e, element e + 16 its high nibble; bit e of qh
+ * is bit 4 of element e's 5-bit number q (reading: the pages name "the qh
+ * word" without a bit order; this is bit e of the little-endian word).  The
+ * element's value is q - 16, in [-16, 15].
+ */
+static int32_t q50_value(const uint8_t *blk, int e) {
+    const uint32_t qh = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8) |
+                        ((uint32_t)blk[2] << 16) | ((uint32_t)blk[3] << 24);
+    const uint8_t byte = blk[4 + (e % 16)];
+    const uint32_t nib = e < 16 ? (byte & 0x0Fu) : (byte >> 4);
+    const uint32_t q = nib | (((qh >> e) & 1u) << 4);
+    return (int32_t)q - 16;
+}
+
+static int32_t q50_block_dot(const int8_t *a, const uint8_t *blk) {
+    int32_t s = 0;
+    for (int e = 0; e < Q8_BLOCK; ++e) s += (int32_t)a[e] * q50_value(blk, e);
+    return s;
+}
+
+/* Decoded Q5_0 values: Wd int8 [N][K] (each in [-16, 15]). */
+int q8o_q50_decode(const uint8_t *W5, int8_t *Wd, int64_t N, int64_t K) {
+    if (N < 0 || K < 0 || K % Q8_BLOCK != 0) return -1;
+    const int64_t KB = K / Q8_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t b = 0; b < KB; ++b)
+            for (int e = 0; e < Q8_BLOCK; ++e)
+                Wd[j * K + b * Q8_BLOCK + e] = (int8_t)q50_value(W5 + (j * KB + b) * 20, e);
+    return 0;
+}
+
+/* Per-block integer partials against Q5_0 weights: int32 [M][N][K/32]. */
+int q8o_q50_block_partials(const int8_t *A, const uint8_t *W5, int32_t *P,
+                           int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0) return -1;
+    const int64_t KB = K / Q8_BLOCK;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            for (int64_t b = 0; b < KB; ++b)
+                P[(i * N + j) * KB + b] =
+                    q50_block_dot(A + i * K + b * Q8_BLOCK, W5 + (j * KB + b) * 20);
+    return 0;
+}
+
+/* One output against Q5_0 weights; ws_t: scales [K/32][N] (q50_qmma_t). */
+static void q50_one(const int8_t *A, const float *AS, const uint8_t *W5,
+                    const float *WS, int ws_t, int64_t i, int64_t j, int64_t N,
+                    int64_t K, double *out, double *abs_terms) {
+    const int64_t KB = K / Q8_BLOCK;
+    double acc = 0.0, mag = 0.0;
+    for (int64_t b = 0; b < KB; ++b) {
+        int32_t p = q50_block_dot(A + i * K + b * Q8_BLOCK, W5 + (j * KB + b) * 20);
+        double ws = ws_t ? (double)WS[b * N + j] : (double)WS[j * KB + b];
+        double term = (double)AS[i * KB + b] * ws * (double)p; /* AS*WS exact */
+        acc += term;
+        mag += fabs(term);
+    }
+    *out = acc;
+    *abs_terms = mag;
+}
+
+/* q50_qdot_t (ws_t == 0, WS [N][K/32]) or q50_qmma_t (ws_t != 0, WS [K/32][N]) in f64. */
+int q8o_q50_f64(const int8_t *A, const float *AS, const uint8_t *W5, const float *WS,
+                int ws_t, int64_t M, int64_t N, int64_t K, double *out, double *abs_terms) {
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            q50_one(A, AS, W5, WS, ws_t, i, j, N, K, out + i * N + j, abs_terms + i * N + j);
+    return 0;
+}
+
+/* The same at `count` sampled output positions (ii[s], jj[s]). */
+int q8o_q50_f64_at(const int8_t *A, const float *AS, const uint8_t *W5, const float *WS,
+                   int ws_t, int64_t M, int64_t N, int64_t K, const int64_t *ii,
+                   const int64_t *jj, int64_t count, double *out, double *abs_terms) {
+    if (M < 0 || N < 0 || K < 0 || K % Q8_BLOCK != 0 || count < 0) return -1;
+    for (int64_t s = 0; s < count; ++s)
+        if (ii[s] < 0 || ii[s] >= M || jj[s] < 0 || jj[s] >= N) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t s = 0; s < count; ++s)
+        q50_one(A, AS, W5, WS, ws_t, ii[s], jj[s], N, K, out + s, abs_terms + s);
     return 0;
 }

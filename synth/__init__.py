@@ -109,3 +109,13 @@ def random_scales(shape, seed: int, lo: float = 1e-3, hi: float = 1e-1) -> np.nd
     rng = np.random.default_rng(seed)
     e = rng.uniform(np.log(lo), np.log(hi), size=shape)
     return np.exp(e).astype(np.float32)
+
+
+def random_q50(rows: int, K: int, seed: int) -> np.ndarray:
+    """Seeded uniform bytes shaped as Q5_0 weight rows, ``uint8 [rows, K/32 * 20]``.
+
+    Every byte pattern is a valid Q5_0 block (qh word + 16 nibble bytes), so
+    uniform bytes give uniform 5-bit codes.
+    """
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 256, size=(rows, K // 32 * 20), dtype=np.uint8)

@@ -30,6 +30,11 @@ MUTANTS = {
     "ties_away_from_zero": ("rintf(xb[t] / scale)", "roundf(xb[t] / scale)"),
     "scale_over_128": ("amax / 127.0f", "amax / 128.0f"),
     "reciprocal_multiply": ("rintf(xb[t] / scale)", "rintf(xb[t] * (1.0f / scale))"),
+    "q50_qh_bit_order_reversed": ("(((qh >> e) & 1u) << 4)", "(((qh >> (31 - e)) & 1u) << 4)"),
+    "q50_nibbles_swapped": ("e < 16 ? (byte & 0x0Fu) : (byte >> 4)", "e < 16 ? (byte >> 4) : (byte & 0x0Fu)"),
+    "q50_no_offset": ("return (int32_t)q - 16;", "return (int32_t)q;"),
+    "q50_qh_big_endian": ("const uint32_t qh = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8) |",
+                          "const uint32_t qh = (uint32_t)blk[3] | ((uint32_t)blk[2] << 8) | 0u * blk[0] |"),
     "qmma_scale_not_transposed": ("(double)WST[b * N + j]", "(double)WST[j * KB + b]"),
     "transposed_weight_operand": ("W + j * K + b * Q8_BLOCK);\n        double s",
                                   "W + (j % 1) * K + b * Q8_BLOCK);\n        double s"),

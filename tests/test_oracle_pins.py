@@ -297,3 +297,84 @@ def test_bad_shapes_rejected():
     with pytest.raises(ValueError):
         oracle.qdot_f64(np.zeros((1, 32), np.int8), np.zeros((1, 2), np.float32),
                         np.zeros((1, 32), np.int8), np.zeros((1, 1), np.float32))
+
+
+# ------------------------------------------------------------------ Q5_0
+
+def _q50_golden():
+    g = json.load(open(os.path.join(GOLDEN, "q50_worked_blocks.json")))
+    W5 = np.frombuffer(bytes.fromhex("".join(g["blocks_hex"])), np.uint8)[None, :].copy()
+    A = np.array(g["A"], np.int8)
+    return g, A, W5
+
+
+def test_q50_golden_worked_blocks():
+    g, A, W5 = _q50_golden()
+    K = g["K"]
+    assert oracle.q50_decode(W5, K)[0].tolist() == g["values"]
+    P = oracle.q50_block_partials(A, W5)
+    assert P[:, 0, :].tolist() == g["P"]
+    ones_a = np.ones((A.shape[0], K // 32), np.float32)
+    ones_w = np.ones((1, K // 32), np.float32)
+    out, mag = oracle.q50_qdot_f64(A, ones_a, W5, ones_w)
+    assert out[:, 0].tolist() == g["out_unit_scales"]
+    out_t, _ = oracle.q50_qmma_f64(A, ones_a, W5, ones_w.T.copy())
+    assert out_t[:, 0].tolist() == g["out_unit_scales"]
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(1, 1, 32, 31), (2, 3, 64, 32), (3, 2, 96, 33)])
+def test_q50_exact_rational_bruteforce(M, N, K, seed):
+    A = synth.random_i8((M, K), seed)
+    W5 = synth.random_q50(N, K, seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 10.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-3, 10.0)
+    KB = K // 32
+    for ws_t in (False, True):
+        W_scales = np.ascontiguousarray(WS.T) if ws_t else WS
+        ex = brute.exact_definition_q50(A, AS, W5, W_scales, ws_t)
+        out, mag = (oracle.q50_qmma_f64 if ws_t else oracle.q50_qdot_f64)(A, AS, W5, W_scales)
+        for i in range(M):
+            for j in range(N):
+                bound = 2.0 * KB * 2.0 ** -53 * float(mag[i, j]) + 1e-300
+                assert abs(out[i, j] - float(ex[i][j])) <= bound
+    # the pure-Python decoder and the oracle's agree value for value
+    Wd = oracle.q50_decode(W5, K)
+    for j in range(N):
+        assert Wd[j].tolist() == brute.q50_values_py(W5[j], K)
+
+
+def test_q50_decode_properties():
+    K = 256
+    W5 = synth.random_q50(40, K, 77)
+    Wd = oracle.q50_decode(W5, K).astype(np.int32)
+    assert Wd.min() >= -16 and Wd.max() <= 15
+    # uniform bytes give every code
+    assert set(np.unique(Wd).tolist()) == set(range(-16, 16))
+    # flipping bit e of a block's qh word moves exactly element e by 16
+    for e in (0, 5, 15, 16, 30, 31):
+        W5b = W5.copy()
+        qh_byte = 20 * 3 + e // 8          # block 3 of every row
+        W5b[:, qh_byte] ^= np.uint8(1 << (e % 8))
+        Wb = oracle.q50_decode(W5b, K).astype(np.int32)
+        diff = Wb - Wd
+        assert (np.abs(diff[:, 96 + e]) == 16).all()
+        diff[:, 96 + e] = 0
+        assert not diff.any()
+    # the nibbles of byte e feed elements e and e + 16 only
+    W5c = W5.copy()
+    W5c[:, 20 * 2 + 4 + 7] ^= np.uint8(0x21)   # block 2, byte 7: low bit 0, high bit 1
+    Wc = oracle.q50_decode(W5c, K).astype(np.int32)
+    d = Wc - Wd
+    assert (np.abs(d[:, 64 + 7]) == 1).all() and (np.abs(d[:, 64 + 23]) == 2).all()
+    d[:, 64 + 7] = 0
+    d[:, 64 + 23] = 0
+    assert not d.any()
+
+
+def test_q50_partials_equal_q8_partials_of_decoded_values():
+    A = synth.random_i8((3, 320), 81)
+    W5 = synth.random_q50(5, 320, 82)
+    P5 = oracle.q50_block_partials(A, W5)
+    P8 = oracle.block_partials(A, oracle.q50_decode(W5, 320))
+    assert np.array_equal(P5, P8)
+    assert np.abs(P5).max() <= 32 * 128 * 16
