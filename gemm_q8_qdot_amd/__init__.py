@@ -29,6 +29,7 @@ Q8_ELAUNCH = -5
 
 # Every symbol include/q8qdot.h declares.
 EXPORTS = ("q8_qdot", "q8_qdot_stream", "q8_qmma", "q8_qdot_partials", "q8_qdot_path",
+           "q8_q50_qdot", "q8_q50_qmma", "q8_q50_partials",
            "q8_quantize", "q8_strerror", "q8_version")
 
 _lock = threading.Lock()
@@ -64,6 +65,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.q8_qdot_stream.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qmma.restype = ci
         lib.q8_qmma.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
+        for name in ("q8_q50_qdot", "q8_q50_qmma"):
+            getattr(lib, name).restype = ci
+            getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
+        lib.q8_q50_partials.restype = ci
+        lib.q8_q50_partials.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qdot_partials.restype = ci
         lib.q8_qdot_partials.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qdot_path.restype = ci
@@ -111,6 +117,17 @@ def q8_qmma_raw(A: int, AS: int, W: int, WST: int, C: int, M: int, N: int, K: in
                 stream: int = 0) -> int:
     """``q8_qmma`` (weight scales ``[K/32, N]``) on raw device addresses; returns the status."""
     return load().q8_qmma(A, AS, W, WST, C, M, N, K, stream or None)
+
+
+def q8_q50_qdot_raw(A: int, AS: int, W5: int, WS: int, C: int, M: int, N: int, K: int,
+                    stream: int = 0, ws_t: bool = False) -> int:
+    """``q8_q50_qdot`` (or, with ``ws_t``, ``q8_q50_qmma``) on raw device addresses."""
+    f = load().q8_q50_qmma if ws_t else load().q8_q50_qdot
+    return f(A, AS, W5, WS, C, M, N, K, stream or None)
+
+
+def q8_q50_partials_raw(A: int, W5: int, P: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return load().q8_q50_partials(A, W5, P, M, N, K, stream or None)
 
 
 def q8_qdot_partials_raw(A: int, W: int, P: int, M: int, N: int, K: int, stream: int = 0) -> int:
@@ -211,6 +228,50 @@ def q8_qdot_partials(A, W, P=None, stream=None):
     s = stream.cuda_stream if stream is not None else _current_stream(A.device)
     st = load().q8_qdot_partials(_ptr(A), _ptr(W), _ptr(P), M, N, K, s or None)
     _check(st, "q8_qdot_partials")
+    return P
+
+
+def _q50_call(A, AS, W5, WS, C, stream, ws_t):
+    torch = _torch()
+    M, K = A.shape
+    N = W5.shape[0]
+    KB = K // 32
+    _need(A, torch.int8, (M, K), "A")
+    _need(AS, torch.float32, (M, KB), "AS")
+    _need(W5, torch.uint8, (N, KB * 20), "W5")
+    _need(WS, torch.float32, (KB, N) if ws_t else (N, KB), "WST" if ws_t else "WS")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _need(C, torch.float32, (M, N), "C")
+    s = stream.cuda_stream if stream is not None else _current_stream(A.device)
+    f = load().q8_q50_qmma if ws_t else load().q8_q50_qdot
+    _check(f(_ptr(A), _ptr(AS), _ptr(W5), _ptr(WS), _ptr(C), M, N, K, s or None),
+           "q8_q50_qmma" if ws_t else "q8_q50_qdot")
+    return C
+
+
+def q8_q50_qdot(A, AS, W5, WS, C=None, stream=None):
+    """``C = q50_qdot_t(A, AS, W5, WS)``: Q5_0 weights ``W5`` uint8 ``[N, K/32*20]``, ``WS [N, K/32]``."""
+    return _q50_call(A, AS, W5, WS, C, stream, False)
+
+
+def q8_q50_qmma(A, AS, W5, WST, C=None, stream=None):
+    """``C = q50_qmma_t(A, AS, W5, WST)``: as :func:`q8_q50_qdot` with ``WST [K/32, N]``."""
+    return _q50_call(A, AS, W5, WST, C, stream, True)
+
+
+def q8_q50_partials(A, W5, P=None, stream=None):
+    """Per-block int32 partials against Q5_0 weights, ``P[M, N, K/32]``."""
+    torch = _torch()
+    M, K = A.shape
+    N = W5.shape[0]
+    _need(A, torch.int8, (M, K), "A")
+    _need(W5, torch.uint8, (N, K // 32 * 20), "W5")
+    if P is None:
+        P = torch.empty((M, N, K // 32), dtype=torch.int32, device=A.device)
+    _need(P, torch.int32, (M, N, K // 32), "P")
+    s = stream.cuda_stream if stream is not None else _current_stream(A.device)
+    _check(load().q8_q50_partials(_ptr(A), _ptr(W5), _ptr(P), M, N, K, s or None), "q8_q50_partials")
     return P
 
 

@@ -17,8 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libq8qdot.so")
 
-SOURCES = ("q8qdot_api.hip", "matvec.hip", "matvec_batch.hip", "qgemm.hip", "qgemm_ksplit.hip",
-           "quantize.hip")
+SOURCES = ("q8qdot_api.hip", "matvec.hip", "matvec_batch.hip", "matvec_q50.hip", "qgemm.hip",
+           "qgemm_ksplit.hip", "quantize.hip")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are disabled for every device pass; hipcc's host

@@ -1,0 +1,155 @@
+// Q5_0-weight matvec for small M (decode step): C[i, :] = q50_qdot_t (or,
+// with transposed weight scales, q50_qmma_t) of activation row i.
+//
+// What is computed: the q50 rows of the Q8_0 table ("Phobos Language Spec",
+// section "Quantized built-ins"): the Q8_0 contraction against a weight held
+// as Q5_0 blocks without their scale -- per 32 values 20 bytes, the qh word
+// then 16 bytes whose byte e holds element e (low nibble) and element e + 16
+// (high nibble); element value q - 16, q the 5-bit number with bit e of qh
+// (little-endian) as bit 4.  Weights cross the bus at 20 bytes per 32 values
+// plus the 4-byte scale ("Quantized built-ins and formats", introduction:
+// decoded in registers).
+//
+// Design for CDNA4 wave64: lane l owns whole blocks b = l + 64 t of a row
+// (one 16-byte and one 4-byte load each; a wave's loads of one t cover 1280
+// contiguous bytes).  The lane's activation bytes for its blocks stay in
+// VGPRs, with their block sums.  Per block: the 5-bit codes q are rebuilt
+// as bytes (nibble | qh bit << 4; four qh bits are spread to four bytes by
+// one 24-bit multiply), eight v_dot4_i32_i8 give sum a*q, and
+// sum a*(q - 16) = sum a*q - 16 * sum a exactly in int32.  A DPP fold sums
+// the row over the wave.
+#include "q8_device.h"
+#include "q8_launch.h"
+
+namespace q8 {
+namespace {
+
+constexpr int kQ5Threads = 256;
+constexpr int kQ5BlockBytes = 20;
+constexpr int kQ5MaxT = 8;               // K <= 64 * 8 blocks (16 Ki values) resident
+constexpr int kQ5MaxWaves = 256 * 32;
+
+// WST: weight scales stored transposed, [K/32][N] (q50_qmma_t).
+template <int T, int R, bool PARTIALS, bool WST>
+__global__ void __launch_bounds__(kQ5Threads)
+matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
+                  const uint8_t* __restrict__ W5, const float* __restrict__ WS,
+                  float* __restrict__ C, int32_t* __restrict__ P, int N, int K) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = blockIdx.x * (kQ5Threads / kWave) + threadIdx.x / kWave;
+    const int nwaves = gridDim.x * (kQ5Threads / kWave);
+    const int i = blockIdx.y;
+    const int KB = K / kBlock;
+    const int64_t row_bytes = (int64_t)KB * kQ5BlockBytes;
+
+    // This lane's activation blocks b = lane + 64 t: bytes, block sums, scales.
+    v4i a_lo[T], a_hi[T];
+    int a_sum[T];
+    float a_s[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int b = lane + kWave * t;
+        const bool ok = b < KB;
+        const int8_t* Ab = A + (int64_t)i * K + (int64_t)b * kBlock;
+        a_lo[t] = ok ? load16(Ab) : v4i{0, 0, 0, 0};
+        a_hi[t] = ok ? load16(Ab + 16) : v4i{0, 0, 0, 0};
+        if constexpr (!PARTIALS) a_s[t] = ok ? AS[(int64_t)i * KB + b] : 0.0f;
+        int s = dot16(a_lo[t], v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101}, 0);
+        a_sum[t] = dot16(a_hi[t], v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101}, s);
+    }
+
+    const int groups = (N + R - 1) / R;
+    for (int g = wave; g < groups; g += nwaves) {
+        const int j0 = g * R;
+        v4i qs[R][T];
+        uint32_t qh[R][T];
+        float ws[R][T];
+        // every load of the row group before the first use
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int j = j0 + r;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int b = lane + kWave * t;
+                const bool ok = j < N && b < KB;
+                const uint8_t* blk = W5 + (int64_t)j * row_bytes + (int64_t)b * kQ5BlockBytes;
+                // the block starts 4-byte aligned: a dword-aligned 16-byte load
+                qh[r][t] = ok ? *reinterpret_cast<const uint32_t*>(blk) : 0u;
+                qs[r][t] = ok ? load16_a4(blk + 4) : v4i{0, 0, 0, 0};
+                if constexpr (!PARTIALS) {
+                    const int64_t widx = WST ? (int64_t)b * N + j : (int64_t)j * KB + b;
+                    ws[r][t] = ok ? WS[widx] : 0.0f;
+                }
+            }
+        }
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                uint32_t q[8];
+                q50_codes(qh[r][t], qs[r][t], q);
+                int d = dot16(a_lo[t], v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]}, 0);
+                d = dot16(a_hi[t], v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]}, d);
+                const int p = d - 16 * a_sum[t];  // sum a * (q - 16), exact
+                if constexpr (PARTIALS) {
+                    const int b = lane + kWave * t;
+                    if (j0 + r < N && b < KB) P[((int64_t)i * N + j0 + r) * KB + b] = p;
+                } else {
+                    acc[r] = fmaf(a_s[t] * ws[r][t], (float)p, acc[r]);
+                }
+            }
+        }
+        if constexpr (!PARTIALS) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float tot = wave_sum(acc[r]);
+                if (lane == 0 && j0 + r < N) C[(int64_t)i * N + j0 + r] = tot;
+            }
+        }
+    }
+}
+
+template <int T, bool PARTIALS, bool WST>
+hipError_t launch_q5_t(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS,
+                       float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    constexpr int R = T == 1 ? 4 : (T == 2 ? 2 : 1);  // short rows: several per wave
+    const int groups = (N + R - 1) / R;
+    const int waves = groups < kQ5MaxWaves ? groups : kQ5MaxWaves;
+    const int wgs = (waves + kQ5Threads / kWave - 1) / (kQ5Threads / kWave);
+    matvec_q50_kernel<T, R, PARTIALS, WST><<<dim3(wgs, M), kQ5Threads, 0, stream>>>(
+        A, AS, W5, WS, C, P, N, K);
+    return hipGetLastError();
+}
+
+template <bool PARTIALS, bool WST>
+hipError_t launch_q5(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS,
+                     float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    const int KB = K / kBlock;
+    const int T = (KB + kWave - 1) / kWave;
+    switch (T) {
+#define Q8_Q5_CASE(T_) \
+    case T_: return launch_q5_t<T_, PARTIALS, WST>(A, AS, W5, WS, C, P, M, N, K, stream);
+        Q8_Q5_CASE(1) Q8_Q5_CASE(2) Q8_Q5_CASE(3) Q8_Q5_CASE(4)
+        Q8_Q5_CASE(5) Q8_Q5_CASE(6) Q8_Q5_CASE(7) Q8_Q5_CASE(8)
+#undef Q8_Q5_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool matvec_q50_fits(int K) { return K <= kQ5MaxT * kWave * kBlock; }
+
+hipError_t launch_matvec_q50(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS,
+                             float* C, int32_t* P, int M, int N, int K, bool ws_t,
+                             hipStream_t stream) {
+    if (!matvec_q50_fits(K)) return hipErrorInvalidValue;
+    if (P != nullptr) return launch_q5<true, false>(A, AS, W5, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_q5<false, true>(A, AS, W5, WS, C, P, M, N, K, stream);
+    return launch_q5<false, false>(A, AS, W5, WS, C, P, M, N, K, stream);
+}
+
+}  // namespace q8

@@ -63,6 +63,14 @@ __device__ __forceinline__ v4i load16(const int8_t* p) {
     return *reinterpret_cast<const v4i*>(p);
 }
 
+// 16 bytes from an address that is only 4-byte aligned (one dword-aligned
+// 16-byte load: the hardware's unaligned-access mode serves it).
+typedef int v4i_a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ v4i load16_a4(const void* p) {
+    const v4i_a4 v = *reinterpret_cast<const v4i_a4*>(p);
+    return v4i{v.x, v.y, v.z, v.w};
+}
+
 __device__ __forceinline__ v4i load16_stream(const int8_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
@@ -111,5 +119,48 @@ __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int v
 // four-byte banks), so the MFMA fragment reads are conflict-free.  swz only
 // depends on r mod 16, so a lane's chunk is the same in every 16-row group.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// ---- Q5_0 weight blocks: 20 bytes per 32 values, the qh word then 16
+// bytes, byte e holding element e (low nibble) and element e + 16 (high);
+// code q = nibble | (bit e of qh) << 4, value q - 16.
+// Four bits of x (bits 0..3) to bit 0 of four bytes: x * (1 + 2^7 + 2^14 +
+// 2^21) places bit i at bit 8 i with no overlapping copies (x < 16).  Both
+// factors fit 24 bits: v_mul_u32_u24 (full rate; the compiler would pick the
+// quarter-rate 32-bit multiply).
+__device__ __forceinline__ uint32_t spread4(uint32_t x) {
+    uint32_t r;
+    asm("v_mul_u32_u24 %0, 0x204081, %1" : "=v"(r) : "v"(x));
+    return r & 0x01010101u;
+}
+
+// The 32 codes q (0..31) of one block as 8 dwords of bytes: elements
+// 4d..4d+3 in q[d], elements 16+4d.. in q[4+d].
+__device__ __forceinline__ void q50_codes(uint32_t qh, const v4i& qs, uint32_t (&q)[8]) {
+    const uint32_t w[4] = {(uint32_t)qs.x, (uint32_t)qs.y, (uint32_t)qs.z, (uint32_t)qs.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = w[d] & 0x0F0F0F0Fu;
+        const uint32_t hi = (w[d] >> 4) & 0x0F0F0F0Fu;
+        q[d] = lo | (spread4(__builtin_amdgcn_ubfe(qh, 4 * d, 4)) << 4);
+        q[4 + d] = hi | (spread4(__builtin_amdgcn_ubfe(qh, 16 + 4 * d, 4)) << 4);
+    }
+}
+
+// The 32 values q - 16 of one block as 8 dwords of signed bytes (same
+// order as q50_codes): value = nibble - 16 when the qh bit is clear, the
+// nibble itself when it is set, i.e. the nibble with 0xF0 or'ed in where
+// the bit is clear (v_perm_b32 selector 0x0C gives byte 0x00, 0x0D 0xFF).
+__device__ __forceinline__ void q50_values(uint32_t qh, const v4i& qs, uint32_t (&v)[8]) {
+    const uint32_t w[4] = {(uint32_t)qs.x, (uint32_t)qs.y, (uint32_t)qs.z, (uint32_t)qs.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = w[d] & 0x0F0F0F0Fu;
+        const uint32_t hi = (w[d] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t sl = 0x0D0D0D0Du - spread4(__builtin_amdgcn_ubfe(qh, 4 * d, 4));
+        const uint32_t sh = 0x0D0D0D0Du - spread4(__builtin_amdgcn_ubfe(qh, 16 + 4 * d, 4));
+        v[d] = (__builtin_amdgcn_perm(0u, 0u, sl) & 0xF0F0F0F0u) | lo;
+        v[4 + d] = (__builtin_amdgcn_perm(0u, 0u, sh) & 0xF0F0F0F0u) | hi;
+    }
+}
 
 }  // namespace q8

@@ -33,6 +33,16 @@ hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W
                                float* C, int32_t* P, int M, int N, int K, bool ws_t,
                                hipStream_t stream);
 
+// Q5_0 weights (W5: 20 bytes per 32 values): one-row matvec for M < 8 with
+// K <= 16 Ki values; otherwise the K-split MFMA GEMM decoding into LDS.
+bool matvec_q50_fits(int K);
+hipError_t launch_matvec_q50(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS,
+                             float* C, int32_t* P, int M, int N, int K, bool ws_t,
+                             hipStream_t stream);
+hipError_t launch_qgemm_ksplit_q50(const int8_t* A, const float* AS, const uint8_t* W5,
+                                   const float* WS, float* C, int32_t* P, int M, int N, int K,
+                                   bool ws_t, hipStream_t stream);
+
 // Q8_0 quantization of f32 rows.
 hipError_t launch_quantize(const float* X, int8_t* Q, float* D, int rows, int K,
                            hipStream_t stream);

@@ -94,6 +94,58 @@ Q8_API int q8_qdot_partials(const int8_t* A, const int8_t* W, int32_t* P, int M,
     return run_qdot(A, nullptr, W, nullptr, nullptr, P, M, N, K, false, static_cast<hipStream_t>(stream));
 }
 
+// Q5_0 weights: W5 is [N][K/32 * 20] bytes, 4-byte aligned (dword loads).
+static int run_q50(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS, float* C,
+            int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
+    int st = check_shape(M, N, K);
+    if (st != Q8_OK) return st;
+    st = check_range(M, N, K, P != nullptr);
+    if (st != Q8_OK) return st;
+    if (M == 0 || N == 0) return Q8_OK;
+    const bool partials = P != nullptr;
+    if (K == 0) {
+        if (partials) return Q8_OK;
+        if (C == nullptr) return Q8_ENULL;
+        if (!aligned(C, 4)) return Q8_EALIGN;
+        return status_of(q8::launch_fill_zero(C, (int64_t)M * N, stream));
+    }
+    const bool matvec = M <= kMatvecMaxM && q8::matvec_q50_fits(K);
+    if (!matvec && (int64_t)K * 32 > INT32_MAX) return Q8_ERANGE;
+    if (!matvec && ws_t && (int64_t)(K / 32) * N * 4 > INT32_MAX) return Q8_ERANGE;
+    if (A == nullptr || W5 == nullptr) return Q8_ENULL;
+    if (!partials && (AS == nullptr || WS == nullptr || C == nullptr)) return Q8_ENULL;
+    if (!aligned(A, 16) || !aligned(W5, 4)) return Q8_EALIGN;
+    if (partials) {
+        if (!aligned(P, 4)) return Q8_EALIGN;
+    } else if (!aligned(AS, 4) || !aligned(WS, 4) || !aligned(C, 4)) {
+        return Q8_EALIGN;
+    }
+    hipError_t e = matvec ? q8::launch_matvec_q50(A, AS, W5, WS, C, P, M, N, K, ws_t, stream)
+                          : q8::launch_qgemm_ksplit_q50(A, AS, W5, WS, C, P, M, N, K, ws_t, stream);
+    return status_of(e);
+}
+
+Q8_API int q8_q50_qdot(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS,
+                       float* C, int M, int N, int K, void* stream) {
+    return run_q50(A, AS, W5, WS, C, nullptr, M, N, K, false, static_cast<hipStream_t>(stream));
+}
+
+Q8_API int q8_q50_qmma(const int8_t* A, const float* AS, const uint8_t* W5, const float* WST,
+                       float* C, int M, int N, int K, void* stream) {
+    return run_q50(A, AS, W5, WST, C, nullptr, M, N, K, true, static_cast<hipStream_t>(stream));
+}
+
+Q8_API int q8_q50_partials(const int8_t* A, const uint8_t* W5, int32_t* P, int M, int N, int K,
+                           void* stream) {
+    if (P == nullptr) {
+        int st = check_shape(M, N, K);
+        if (st != Q8_OK) return st;
+        if (M == 0 || N == 0 || K == 0) return Q8_OK;
+        return Q8_ENULL;
+    }
+    return run_q50(A, nullptr, W5, nullptr, nullptr, P, M, N, K, false, static_cast<hipStream_t>(stream));
+}
+
 Q8_API int q8_qdot_path(int M, int N, int K) {
     int st = check_shape(M, N, K);
     if (st != Q8_OK) return st;
@@ -114,7 +166,7 @@ Q8_API const char* q8_strerror(int status) {
         case Q8_OK: return "ok";
         case Q8_EINVAL: return "invalid shape: M, N, K must be >= 0 and K a multiple of 32";
         case Q8_ENULL: return "null pointer for an operand the call must dereference";
-        case Q8_EALIGN: return "misaligned pointer: A, W, X, Q need 16 bytes, f32/int32 arrays 4";
+        case Q8_EALIGN: return "misaligned pointer: A, W, X, Q need 16 bytes, Q5_0 weights and f32/int32 arrays 4";
         case Q8_ERANGE: return "extent product overflows 64-bit addressing";
         case Q8_ELAUNCH: return "HIP runtime rejected the kernel launch";
         default: return "unknown status";

@@ -65,13 +65,19 @@ constexpr size_t ksplit_smem_bytes() {
 // A chunk's operands as loaded: lane l holds 16 bytes of rows 8q + l/8
 // (q = 0..3), chunk l % 8, and the scales of rows l/4 and 16 + l/4,
 // block l % 4.
+// Q5_0 weights: lane l holds blocks (row (l + 64 h) / 4, block (l + 64 h) % 4)
+// of the chunk, h = 0, 1: the qh word and the 16 nibble bytes.
 struct KsRaw {
     v4i a[4], w[4];
     float as[2], ws[2];
+    uint32_t qh[2];
+    v4i qs[2];
 };
 
 // WST: weight scales stored transposed, [K/32][N] (the qmma_t form).
-template <int NW, bool PF, bool PARTIALS, bool WST>
+// Q5: W holds Q5_0 blocks (20 bytes per 32 values; the q50 rows of the
+// Q8_0 table), decoded to signed bytes on their way into LDS.
+template <int NW, bool PF, bool PARTIALS, bool WST, bool Q5>
 __global__ void __launch_bounds__(NW * kWave)
 qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -99,7 +105,7 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const int rows_a = M - i0 < kTile ? (int)(M - i0) : kTile;
     const int rows_w = N - j0 < kTile ? (int)(N - j0) : kTile;
     const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A + i0 * K, (int64_t)rows_a * K);
-    const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(W + j0 * K, (int64_t)rows_w * K);
+    const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(Q5 ? W : W + j0 * K, Q5 ? 0 : (int64_t)rows_w * K);
     // (the debug entry passes no scales and reads none)
     const __amdgpu_buffer_rsrc_t rAS = buffer_rsrc(PARTIALS ? nullptr : AS + i0 * KB, (int64_t)rows_a * KB * 4);
     // Weight scales [N][K/32]: this tile's rows.  Transposed [K/32][N]: from
@@ -129,7 +135,21 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         for (int q = 0; q < 4; ++q) {
             const int v = vo == kNoRead ? kNoRead : vo + 8 * q * K;
             raw.a[q] = buffer_load16(rA, v, so);
-            raw.w[q] = buffer_load16(rW, v, so);
+            if constexpr (!Q5) raw.w[q] = buffer_load16(rW, v, so);
+        }
+        if constexpr (Q5) {
+            // whole blocks per lane; rows past N and blocks past K load
+            // nothing (their values meet no stored output / are skipped)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int idx = lane + kWave * h;
+                const int64_t j = j0 + idx / 4;
+                const int b = kb0 + idx % 4;
+                const bool ok = j < N && b < KB;
+                const int8_t* blk = W + (ok ? j * KB * 20 + (int64_t)b * 20 : 0);
+                raw.qh[h] = ok ? *reinterpret_cast<const uint32_t*>(blk) : 0u;
+                raw.qs[h] = ok ? load16_a4(blk + 4) : v4i{0, 0, 0, 0};
+            }
         }
         if constexpr (!PARTIALS) {
             const bool blk_ok = kb0 + sblk < KB;
@@ -167,7 +187,21 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             const int row = 8 * q + lrow;
             const int off = row * kKsSeg + 16 * (lch ^ swz(row));
             *reinterpret_cast<v4i*>(st.a + off) = raw.a[q];
-            *reinterpret_cast<v4i*>(st.w + off) = raw.w[q];
+            if constexpr (!Q5) *reinterpret_cast<v4i*>(st.w + off) = raw.w[q];
+        }
+        if constexpr (Q5) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int idx = lane + kWave * h;
+                const int row = idx / 4, blk = idx % 4;
+                uint32_t v[8];
+                q50_values(raw.qh[h], raw.qs[h], v);
+                // logical chunks 2 blk (values 0..15) and 2 blk + 1 (16..31)
+                *reinterpret_cast<v4i*>(st.w + row * kKsSeg + 16 * ((2 * blk) ^ swz(row))) =
+                    v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+                *reinterpret_cast<v4i*>(st.w + row * kKsSeg + 16 * ((2 * blk + 1) ^ swz(row))) =
+                    v4i{(int)v[4], (int)v[5], (int)v[6], (int)v[7]};
+            }
         }
         if constexpr (!PARTIALS) {
 #pragma unroll
@@ -257,7 +291,7 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     }
 }
 
-template <int NW, bool PF, bool PARTIALS, bool WST>
+template <int NW, bool PF, bool PARTIALS, bool WST, bool Q5>
 hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                      float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     const int64_t m_tiles = (M + kTile - 1) / kTile;
@@ -266,7 +300,7 @@ hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const fl
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     constexpr size_t smem = ksplit_smem_bytes<NW>();
     static_assert(smem <= 160 * 1024, "LDS budget");
-    auto kern = qgemm_ksplit_kernel<NW, PF, PARTIALS, WST>;
+    auto kern = qgemm_ksplit_kernel<NW, PF, PARTIALS, WST, Q5>;
     if (smem > 64 * 1024) {
         static bool attr_set = false;
         if (!attr_set) {
@@ -287,9 +321,19 @@ hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W
                                float* C, int32_t* P, int M, int N, int K, bool ws_t,
                                hipStream_t stream) {
     constexpr bool pf = Q8_KS_PREFETCH != 0;
-    if (P != nullptr) return launch_ks<kKsWaves, pf, true, false>(A, AS, W, WS, C, P, M, N, K, stream);
-    if (ws_t) return launch_ks<kKsWaves, pf, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_ks<kKsWaves, pf, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (P != nullptr) return launch_ks<kKsWaves, pf, true, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_ks<kKsWaves, pf, false, true, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks<kKsWaves, pf, false, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
+}
+
+hipError_t launch_qgemm_ksplit_q50(const int8_t* A, const float* AS, const uint8_t* W5,
+                                   const float* WS, float* C, int32_t* P, int M, int N, int K,
+                                   bool ws_t, hipStream_t stream) {
+    constexpr bool pf = Q8_KS_PREFETCH != 0;
+    const int8_t* W = reinterpret_cast<const int8_t*>(W5);
+    if (P != nullptr) return launch_ks<kKsWaves, pf, true, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_ks<kKsWaves, pf, false, true, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks<kKsWaves, pf, false, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 }  // namespace q8

@@ -57,7 +57,7 @@ typedef enum {
     Q8_OK = 0,
     Q8_EINVAL = -1,  /* M, N or K negative, or K % 32 != 0 */
     Q8_ENULL = -2,   /* a pointer the call must dereference is NULL */
-    Q8_EALIGN = -3,  /* A/W/X/Q not 16-byte aligned, or another array not 4-byte aligned */
+    Q8_EALIGN = -3,  /* A/W/X/Q not 16-byte aligned, or W5 or another array not 4-byte aligned */
     Q8_ERANGE = -4,  /* an extent product overflows 64-bit byte addressing, or
                         M >= 8 with 32 * K > 2^31 - 1 (32-bit tile offsets), or
                         q8_qmma with M >= 8 and (K/32) * N * 4 > 2^31 - 1 */
@@ -92,6 +92,34 @@ int q8_qdot_stream(const int8_t *A, const float *AS, const int8_t *W, const floa
  */
 int q8_qmma(const int8_t *A, const float *AS, const int8_t *W, const float *WST,
             float *C, int M, int N, int K, void *stream);
+
+/*
+ * Q5_0 weights ("Phobos Language Spec", section "Quantized built-ins", Q8_0
+ * table, rows q50_qdot_t and q50_qmma_t; "Quantized built-ins and formats",
+ * section "Q8_0"): the same contraction against a weight held as Q5_0 blocks
+ * without their scale.
+ *
+ *     W5  uint8 [N][K/32 * 20]  per 32 values: the qh word (4 bytes,
+ *                               little-endian), then 16 bytes; byte e holds
+ *                               element e in its low nibble and element e+16
+ *                               in its high nibble; the element is q - 16,
+ *                               q = nibble + 16 * (bit e of qh)
+ *
+ * (The bit of qh that belongs to element e is not stated on the pages; this
+ * library reads it as bit e of the little-endian word.)  W5 must be 4-byte
+ * aligned; A 16-byte; AS, WS/WST, C, P 4-byte.  Scales as for q8_qdot_stream
+ * (q8_q50_qdot: WS [N][K/32]) and q8_qmma (q8_q50_qmma: WST [K/32][N]).
+ * M < 8 with K <= 16384 runs a one-row matvec per activation row; anything
+ * else the K-split MFMA GEMM (for which 32 * K, and with WST (K/32) * N * 4,
+ * must be below 2^31, else Q8_ERANGE).  q8_q50_partials: P[i][j][b] =
+ * sum over the block of A * (q - 16), int32 [M][N][K/32].
+ */
+int q8_q50_qdot(const int8_t *A, const float *AS, const uint8_t *W5, const float *WS,
+                float *C, int M, int N, int K, void *stream);
+int q8_q50_qmma(const int8_t *A, const float *AS, const uint8_t *W5, const float *WST,
+                float *C, int M, int N, int K, void *stream);
+int q8_q50_partials(const int8_t *A, const uint8_t *W5, int32_t *P, int M, int N, int K,
+                    void *stream);
 
 /*
  * Debug entry: P[i][j][b] = the int32 block sum of the qdot_t definition,

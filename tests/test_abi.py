@@ -25,7 +25,7 @@ def lib():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q8_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_expected_entry_points():
@@ -113,6 +113,24 @@ def test_empty_outputs_are_noops(lib):
     assert q8.q8_quantize_raw(0, 0, 0, 0, 64) == q8.Q8_OK
     assert q8.q8_quantize_raw(0, 0, 0, 4, 0) == q8.Q8_OK
     assert q8.q8_quantize_raw(0, 0, 0, 1, 33) == q8.Q8_EINVAL
+
+
+def test_q50_validation(lib):
+    ok = 4096
+    base = 1 << 20
+    for ws_t in (False, True):
+        # bad shapes, nulls, alignment (W5 needs 4 bytes, A 16)
+        assert q8.q8_q50_qdot_raw(16, 16, 16, 16, 16, 2, 2, 48, ws_t=ws_t) == q8.Q8_EINVAL
+        assert q8.q8_q50_qdot_raw(0, ok, ok, ok, ok, 1, 64, 64, ws_t=ws_t) == q8.Q8_ENULL
+        assert q8.q8_q50_qdot_raw(ok, ok, 0, ok, ok, 9, 64, 64, ws_t=ws_t) == q8.Q8_ENULL
+        assert q8.q8_q50_qdot_raw(base, base, base + 2, base, base, 1, 4, 32, ws_t=ws_t) == q8.Q8_EALIGN
+        assert q8.q8_q50_qdot_raw(base + 4, base, base, base, base, 9, 4, 32, ws_t=ws_t) == q8.Q8_EALIGN
+        assert q8.q8_q50_qdot_raw(0, 0, 0, 0, 0, 0, 4, 32, ws_t=ws_t) == q8.Q8_OK
+    assert q8.q8_q50_partials_raw(16, 16, 0, 8, 8, 64) == q8.Q8_ENULL
+    assert q8.q8_q50_partials_raw(base, base + 1, base, 8, 8, 64) == q8.Q8_EALIGN
+    assert q8.q8_q50_partials_raw(0, 0, 0, 3, 3, 0) == q8.Q8_OK
+    # the GEMM path addresses tiles with 32-bit offsets
+    assert q8.q8_q50_qdot_raw(16, 16, 16, 16, 16, 8, 4, 2**26) == q8.Q8_ERANGE
 
 
 def test_range_overflow_rejected(lib):
