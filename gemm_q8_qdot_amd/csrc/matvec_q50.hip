@@ -10,10 +10,10 @@
 // plus the 4-byte scale ("Quantized built-ins and formats", introduction:
 // decoded in registers).
 //
-// Design for CDNA4 wave64: lane l owns whole blocks b = l + 64 t of a row
-// (one 16-byte and one 4-byte load each; a wave's loads of one t cover 1280
-// contiguous bytes).  The lane's activation bytes for its blocks stay in
-// VGPRs, with their block sums.  Per block: the 5-bit codes q are rebuilt
+// Design for CDNA4 wave64: lane l owns whole blocks b = l + 64 t of a row;
+// the rows arrive as contiguous 1 KiB wave loads staged in LDS (see the
+// kernel).  The lane's activation bytes for its blocks stay in VGPRs, with
+// their block sums.  Per block: the 5-bit codes q are rebuilt
 // as bytes (nibble | qh bit << 4; four qh bits are spread to four bytes by
 // one 24-bit multiply), eight v_dot4_i32_i8 give sum a*q, and
 // sum a*(q - 16) = sum a*q - 16 * sum a exactly in int32.  A DPP fold sums
@@ -27,20 +27,43 @@ namespace {
 constexpr int kQ5Threads = 256;
 constexpr int kQ5BlockBytes = 20;
 constexpr int kQ5MaxT = 8;               // K <= 64 * 8 blocks (16 Ki values) resident
-constexpr int kQ5MaxWaves = 256 * 32;
+constexpr int kQ5MaxWaves = 256 * 8;     // eight waves per CU, each walking several row groups
 
 // WST: weight scales stored transposed, [K/32][N] (q50_qmma_t).
+// A wave reads its R weight rows as contiguous 16-byte pieces (lane l takes
+// bytes [16 (l + 64 s), +16) of the rows' bytes: full 1 KiB transactions),
+// parks them in its own LDS area, and each lane then reads back its whole
+// 20-byte blocks (5-dword stride across lanes: no bank conflicts).  The
+// weight array is read through a raw buffer resource, so pieces past its
+// end read as zero.
 template <int T, int R, bool PARTIALS, bool WST>
 __global__ void __launch_bounds__(kQ5Threads)
 matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                   const uint8_t* __restrict__ W5, const float* __restrict__ WS,
                   float* __restrict__ C, int32_t* __restrict__ P, int N, int K) {
+    extern __shared__ __align__(16) uint8_t q5_smem[];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = blockIdx.x * (kQ5Threads / kWave) + threadIdx.x / kWave;
+    const int wv = threadIdx.x / kWave;
+    const int wave = blockIdx.x * (kQ5Threads / kWave) + wv;
     const int nwaves = gridDim.x * (kQ5Threads / kWave);
     const int i = blockIdx.y;
     const int KB = K / kBlock;
-    const int64_t row_bytes = (int64_t)KB * kQ5BlockBytes;
+    const int row_bytes = KB * kQ5BlockBytes;
+    const int group_bytes = R * row_bytes;            // this wave's rows, contiguous in W5
+    const int pieces = (group_bytes + 15) / 16;       // 16-byte pieces of the group
+    constexpr int kPieceRounds = (R * T * kWave * kQ5BlockBytes + kWave * 16 - 1) / (kWave * 16);
+    uint8_t* area = q5_smem + (size_t)wv * kPieceRounds * kWave * 16;
+    int8_t* a_lds = reinterpret_cast<int8_t*>(q5_smem + (size_t)(kQ5Threads / kWave) * kPieceRounds * kWave * 16);
+    float* as_lds = reinterpret_cast<float*>(a_lds + K);
+    const __amdgpu_buffer_rsrc_t rW5 = buffer_rsrc(W5, (int64_t)N * row_bytes);
+
+    // The activation row and its scales, read once per workgroup (not once
+    // per wave) and shared through LDS.
+    for (int idx = threadIdx.x * 16; idx < K; idx += kQ5Threads * 16)
+        *reinterpret_cast<v4i*>(a_lds + idx) = load16(A + (int64_t)i * K + idx);
+    if constexpr (!PARTIALS)
+        for (int idx = threadIdx.x; idx < KB; idx += kQ5Threads) as_lds[idx] = AS[(int64_t)i * KB + idx];
+    __syncthreads();
 
     // This lane's activation blocks b = lane + 64 t: bytes, block sums, scales.
     v4i a_lo[T], a_hi[T];
@@ -50,38 +73,51 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     for (int t = 0; t < T; ++t) {
         const int b = lane + kWave * t;
         const bool ok = b < KB;
-        const int8_t* Ab = A + (int64_t)i * K + (int64_t)b * kBlock;
-        a_lo[t] = ok ? load16(Ab) : v4i{0, 0, 0, 0};
-        a_hi[t] = ok ? load16(Ab + 16) : v4i{0, 0, 0, 0};
-        if constexpr (!PARTIALS) a_s[t] = ok ? AS[(int64_t)i * KB + b] : 0.0f;
+        const int8_t* Ab = a_lds + (ok ? b : 0) * kBlock;
+        a_lo[t] = ok ? *reinterpret_cast<const v4i*>(Ab) : v4i{0, 0, 0, 0};
+        a_hi[t] = ok ? *reinterpret_cast<const v4i*>(Ab + 16) : v4i{0, 0, 0, 0};
+        if constexpr (!PARTIALS) a_s[t] = ok ? as_lds[b] : 0.0f;
         int s = dot16(a_lo[t], v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101}, 0);
         a_sum[t] = dot16(a_hi[t], v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101}, s);
     }
 
     const int groups = (N + R - 1) / R;
+    // A group's bytes: contiguous 16-byte pieces (the resource zeroes pieces
+    // past the array; pieces past the group are not needed).  The next
+    // group's pieces are loaded into registers while this group, already
+    // parked in LDS, is decoded and computed.
+    v4i piece[kPieceRounds];
+    auto load_group = [&](int g) {
+        const int gbase = g * R * row_bytes;
+#pragma unroll
+        for (int s = 0; s < kPieceRounds; ++s) {
+            const int pc = lane + kWave * s;
+            piece[s] = buffer_load16(rW5, pc < pieces ? gbase + 16 * pc : kNoRead, 0);
+        }
+    };
+    if (wave < groups) load_group(wave);
     for (int g = wave; g < groups; g += nwaves) {
         const int j0 = g * R;
-        v4i qs[R][T];
-        uint32_t qh[R][T];
         float ws[R][T];
-        // every load of the row group before the first use
+        if constexpr (!PARTIALS) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int j = j0 + r;
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int b = lane + kWave * t;
-                const bool ok = j < N && b < KB;
-                const uint8_t* blk = W5 + (int64_t)j * row_bytes + (int64_t)b * kQ5BlockBytes;
-                // the block starts 4-byte aligned: a dword-aligned 16-byte load
-                qh[r][t] = ok ? *reinterpret_cast<const uint32_t*>(blk) : 0u;
-                qs[r][t] = ok ? load16_a4(blk + 4) : v4i{0, 0, 0, 0};
-                if constexpr (!PARTIALS) {
+                for (int t = 0; t < T; ++t) {
+                    const int j = j0 + r;
+                    const int b = lane + kWave * t;
                     const int64_t widx = WST ? (int64_t)b * N + j : (int64_t)j * KB + b;
-                    ws[r][t] = ok ? WS[widx] : 0.0f;
+                    ws[r][t] = (j < N && b < KB) ? WS[widx] : 0.0f;
                 }
-            }
         }
+        // The previous group's reads of this area are done (one wave, in order).
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int s = 0; s < kPieceRounds; ++s)
+            *reinterpret_cast<v4i*>(area + 16 * (lane + kWave * s)) = piece[s];
+        asm volatile("" ::: "memory");
+        if (g + nwaves < groups) load_group(g + nwaves);
+
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.0f;
@@ -89,13 +125,17 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         for (int r = 0; r < R; ++r) {
 #pragma unroll
             for (int t = 0; t < T; ++t) {
+                const int b = lane + kWave * t;
+                const uint32_t* blk = reinterpret_cast<const uint32_t*>(
+                    area + r * row_bytes + (b < KB ? b : 0) * kQ5BlockBytes);
+                const uint32_t qh = blk[0];
+                const v4i qs = v4i{(int)blk[1], (int)blk[2], (int)blk[3], (int)blk[4]};
                 uint32_t q[8];
-                q50_codes(qh[r][t], qs[r][t], q);
+                q50_codes(qh, qs, q);
                 int d = dot16(a_lo[t], v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]}, 0);
                 d = dot16(a_hi[t], v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]}, d);
                 const int p = d - 16 * a_sum[t];  // sum a * (q - 16), exact
                 if constexpr (PARTIALS) {
-                    const int b = lane + kWave * t;
                     if (j0 + r < N && b < KB) P[((int64_t)i * N + j0 + r) * KB + b] = p;
                 } else {
                     acc[r] = fmaf(a_s[t] * ws[r][t], (float)p, acc[r]);
@@ -116,10 +156,14 @@ template <int T, bool PARTIALS, bool WST>
 hipError_t launch_q5_t(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS,
                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     constexpr int R = T == 1 ? 4 : (T == 2 ? 2 : 1);  // short rows: several per wave
+    constexpr int kPieceRounds = (R * T * kWave * kQ5BlockBytes + kWave * 16 - 1) / (kWave * 16);
+    // per-wave weight staging areas, then the activation row and its scales
+    const size_t smem = (size_t)(kQ5Threads / kWave) * kPieceRounds * kWave * 16 + (size_t)K +
+                        (size_t)(K / kBlock) * 4;
     const int groups = (N + R - 1) / R;
     const int waves = groups < kQ5MaxWaves ? groups : kQ5MaxWaves;
     const int wgs = (waves + kQ5Threads / kWave - 1) / (kQ5Threads / kWave);
-    matvec_q50_kernel<T, R, PARTIALS, WST><<<dim3(wgs, M), kQ5Threads, 0, stream>>>(
+    matvec_q50_kernel<T, R, PARTIALS, WST><<<dim3(wgs, M), kQ5Threads, smem, stream>>>(
         A, AS, W5, WS, C, P, N, K);
     return hipGetLastError();
 }

@@ -109,7 +109,9 @@ static int run_q50(const int8_t* A, const float* AS, const uint8_t* W5, const fl
         if (!aligned(C, 4)) return Q8_EALIGN;
         return status_of(q8::launch_fill_zero(C, (int64_t)M * N, stream));
     }
-    const bool matvec = M <= kMatvecMaxM && q8::matvec_q50_fits(K);
+    // The matvec addresses the whole weight array with 32-bit offsets.
+    const bool matvec = M <= kMatvecMaxM && q8::matvec_q50_fits(K) &&
+                        (int64_t)N * (K / 32) * 20 < INT32_MAX - (1 << 20);
     if (!matvec && (int64_t)K * 32 > INT32_MAX) return Q8_ERANGE;
     if (!matvec && ws_t && (int64_t)(K / 32) * N * 4 > INT32_MAX) return Q8_ERANGE;
     if (A == nullptr || W5 == nullptr) return Q8_ENULL;
