@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=1, help="index into synth.WORKLOADS for the headline")
     ap.add_argument("--second", type=int, default=4, help="second measured workload (-1: none)")
     ap.add_argument("--others", default="0,2,3", help="other workloads timed briefly ('' for none)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the qmma_t / Q5_0 / small-batch timings")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
     ap.add_argument("--no-rotate", action="store_true", help="reuse one copy (cache-warm number)")
     ap.add_argument("--profile", action="store_true",
@@ -64,10 +66,16 @@ def parse():
 
 
 class Operands:
-    """R device copies of (A, AS, W, WS, C) for one workload, quantized on the GPU."""
+    """R device copies of (A, AS, W, WS, C) for one workload, quantized on the GPU.
 
-    def __init__(self, torch, q8, w: synth.Workload, rotate: bool):
+    ``kind``: "qdot" (W int8, WS [N, K/32]), "qmma" (the same weights, scales
+    stored [K/32, N]) or "q50" (W as Q5_0 blocks, 20 bytes per 32 values,
+    seeded uniform codes; scales from the Q8_0 quantization of the weights).
+    """
+
+    def __init__(self, torch, q8, w: synth.Workload, rotate: bool, kind: str = "qdot"):
         self.w = w
+        self.kind = kind
         dev = torch.device("cuda:0")
         a32, w32 = synth.workload_f32(w)
         Xa = torch.from_numpy(a32).to(dev)
@@ -75,6 +83,10 @@ class Operands:
         A, AS = q8.q8_quantize(Xa)
         W, WS = q8.q8_quantize(Xw)
         del Xa, Xw
+        if kind == "qmma":
+            WS = WS.t().contiguous()
+        elif kind == "q50":
+            W = torch.from_numpy(synth.random_q50(w.N, w.K, 4000 + w.index)).to(dev)
         per_copy = A.numel() + AS.numel() * 4 + W.numel() + WS.numel() * 4 + w.M * w.N * 4
         self.R = max(1, -(-CACHE_DEFEAT_BYTES // per_copy)) if rotate else 1
         self.copies = []
@@ -100,12 +112,12 @@ def time_launches(torch, q8, ops: Operands, steps: int, warmup: int):
     sptr = stream.cuda_stream
     cps = ops.copies
     w = ops.w
-    raw = q8.q8_qdot_raw
+    raw = {"qdot": q8.q8_qdot_raw, "qmma": q8.q8_qmma_raw, "q50": q8.q8_q50_qdot_raw}[ops.kind]
     ptrs = [(a.data_ptr(), s.data_ptr(), b.data_ptr(), t.data_ptr(), c.data_ptr()) for a, s, b, t, c in cps]
     for k in range(warmup):
         st = raw(*ptrs[k % len(ptrs)], w.M, w.N, w.K, sptr)
         if st:
-            raise RuntimeError("q8_qdot failed: %s" % q8.q8_strerror(st))
+            raise RuntimeError("%s failed: %s" % (ops.kind, q8.q8_strerror(st)))
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -304,6 +316,32 @@ def main():
         result["others"].append(rec)
         log("[bench] %s: %.3f us/launch, %.1f GB/s (%.1f%% HBM), %.1f int8 TOPS"
             % (ow.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"], rec["int8_tops"]))
+        del ops
+        torch.cuda.empty_cache()
+
+    # The other entry points and dispatch paths, on the same workload shapes:
+    # qmma_t (transposed scales), Q5_0 weights, and a small decode batch.
+    variants = [] if (args.no_variants or args.profile) else [
+        ("qmma", synth.WORKLOADS[1]), ("qmma", synth.WORKLOADS[4]),
+        ("q50", synth.WORKLOADS[1]), ("q50", synth.WORKLOADS[2]), ("q50", synth.WORKLOADS[3]),
+        ("qdot", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
+    ]
+    if variants:
+        result["variants"] = []
+    for kind, vw in variants:
+        ops = Operands(torch, q8, vw, rotate=not args.no_rotate, kind=kind)
+        ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
+        rec = {"entry": {"qdot": "q8_qdot", "qmma": "q8_qmma", "q50": "q8_q50_qdot"}[kind],
+               "workload": vw.name, "M": vw.M, "N": vw.N, "K": vw.K,
+               "us_per_launch": round(ms3 * 1e3, 3),
+               "weight_bytes": ops.weight_bytes,
+               "hbm_gbs": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9, 1),
+               "hbm_frac": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "int8_tops": round(ops.int8_ops / (ms3 * 1e-3) / 1e12, 2)}
+        result["variants"].append(rec)
+        log("[bench] %s %s: %.3f us/launch, %.1f GB/s (%.1f%% HBM), %.1f int8 TOPS"
+            % (rec["entry"], vw.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"],
+               rec["int8_tops"]))
         del ops
         torch.cuda.empty_cache()
 
