@@ -22,6 +22,11 @@
 //     when K <= 16 KiB (else they are re-read per chunk); the activation scale
 //     is zeroed in odd lanes so each block is scaled and accumulated once;
 //   - the f32 accumulator is folded across the wave with DPP (no LDS).
+// Two kernels share this scheme: matvec_rows_kernel (one activation row,
+// K <= 16 KiB, weight scales [N][K/32]: the decode case, with row-sized
+// buffer resources and a launch of one workgroup per compute unit) and
+// matvec_kernel (transposed weight scales, which it stages through LDS per
+// workgroup, and rows longer than 16 KiB, taken in 16 KiB chunks).
 // HBM-bound: algorithmic traffic is N*K weight bytes + N*K/8 scale bytes.
 #include "q8_device.h"
 #include "q8_launch.h"
@@ -187,6 +192,131 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     }
 }
 
+// ---- One activation row, K <= 16 KiB: the main decode kernel.
+// A wave holds its lanes' slice of the activation row (and scales) in VGPRs
+// and walks weight rows with a grid stride.  Each row is read through a
+// buffer resource built for that row alone (its base is wave-uniform, so the
+// resource sits in SGPRs): a lane's offset past K, or a row past N, reads
+// zero, so there are no lane masks and no 64-bit address arithmetic, and the
+// whole wave fits in few VGPRs.  Launch shape, measured on MI355X: rows of up
+// to 8 KiB run one 8-wave workgroup per compute unit; longer rows run one
+// 4-wave workgroup per compute unit with the next row's loads issued before
+// the current row is computed (PF).  Fewer bytes in flight per compute unit
+// than either made the stream slower; more (more waves, or several
+// workgroups per compute unit) made it slower too.
+template <int S, bool PF, bool PARTIALS, int T>
+__global__ void __launch_bounds__(T)
+matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
+                   const int8_t* __restrict__ W, const float* __restrict__ WS,
+                   float* __restrict__ C, int32_t* __restrict__ P, int N, int K) {
+    const int lane = threadIdx.x & (kWave - 1);
+    // wave-uniform (readfirstlane), so the row resources live in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (T / kWave) + (int)(threadIdx.x / kWave));
+    const int nwaves = gridDim.x * (T / kWave);
+    const int i = blockIdx.y;
+    const int KB = K / kBlock;
+    const bool even = (lane & 1) == 0;
+    const int lo = lane * 16;
+
+    // This lane's activation bytes [1024 s + 16 lane, +16) and, in even
+    // lanes, the scale of their block (odd lanes hold 0: each block's
+    // product is accumulated once).
+    const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A + (int64_t)i * K, K);
+    const __amdgpu_buffer_rsrc_t rAS = buffer_rsrc(AS + (int64_t)i * KB, (int64_t)KB * 4);
+    v4i a[S];
+    float as[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int off = s * kStepBytes + lo;
+        a[s] = buffer_load16(rA, off < K ? off : kNoRead, 0);
+        if constexpr (!PARTIALS)
+            as[s] = buffer_load_f32(rAS, (even && off < K) ? (off / kBlock) * 4 : kNoRead, 0);
+    }
+
+    auto load_row = [&](int j, v4i (&w)[S], float (&ws)[S]) {
+        const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(W + (int64_t)j * K, K);
+        const __amdgpu_buffer_rsrc_t rWS = buffer_rsrc(WS + (int64_t)j * KB, (int64_t)KB * 4);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int off = s * kStepBytes + lo;
+            w[s] = buffer_load16_nt(rW, off < K ? off : kNoRead, 0);  // read once: streaming
+            if constexpr (!PARTIALS) ws[s] = buffer_load_f32(rWS, off < K ? (off / kBlock) * 4 : kNoRead, 0);
+        }
+    };
+    auto compute_row = [&](int j, const v4i (&w)[S], const float (&ws)[S]) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            int p = dot16(a[s], w[s], 0);
+            p += dpp_i32<kDppSwapPairs>(p);  // exact block sum in both lanes of the pair
+            if constexpr (PARTIALS) {
+                const int off = s * kStepBytes + lo;
+                if (even && off < K) P[((int64_t)i * N + j) * KB + off / kBlock] = p;
+            } else {
+                acc = fmaf(as[s] * ws[s], (float)p, acc);
+            }
+        }
+        if constexpr (!PARTIALS) {
+            const float tot = wave_sum(acc);
+            if (lane == 0) C[(int64_t)i * N + j] = tot;
+        }
+    };
+
+    if constexpr (PF) {
+        // Two rows in flight: ping-pong registers, loop unrolled by two.
+        v4i w0[S], w1[S];
+        float ws0[S], ws1[S];
+        int j = wave;
+        if (j < N) load_row(j, w0, ws0);
+        while (j < N) {
+            const int j1 = j + nwaves;
+            if (j1 < N) load_row(j1, w1, ws1);
+            compute_row(j, w0, ws0);
+            if (j1 >= N) break;
+            const int j2 = j1 + nwaves;
+            if (j2 < N) load_row(j2, w0, ws0);
+            compute_row(j1, w1, ws1);
+            j = j2;
+        }
+    } else {
+        for (int j = wave; j < N; j += nwaves) {
+            v4i w[S];
+            float ws[S];
+            load_row(j, w, ws);
+            compute_row(j, w, ws);
+        }
+    }
+}
+
+template <int S, bool PARTIALS>
+hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                       float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    // Prefetch for rows of 9..14 KiB (two rows of 15 or 16 KiB in registers
+    // would spill).
+    constexpr bool kPF = S > 8 && S <= 14;
+    constexpr int kT = kPF ? 256 : 512;
+    const int cap = device_cu_count() * (kT / kWave);
+    const int waves = N < cap ? N : cap;
+    const int wgs = (waves + kT / kWave - 1) / (kT / kWave);
+    matvec_rows_kernel<S, kPF, PARTIALS, kT><<<dim3(wgs, M), kT, 0, stream>>>(A, AS, W, WS, C, P, N, K);
+    return hipGetLastError();
+}
+
+template <bool PARTIALS>
+hipError_t launch_rows_any(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                           float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    switch ((K + kStepBytes - 1) / kStepBytes) {
+#define Q8_ROWS_CASE(S_) \
+    case S_: return launch_rows<S_, PARTIALS>(A, AS, W, WS, C, P, M, N, K, stream);
+        Q8_ROWS_CASE(1) Q8_ROWS_CASE(2) Q8_ROWS_CASE(3) Q8_ROWS_CASE(4)
+        Q8_ROWS_CASE(5) Q8_ROWS_CASE(6) Q8_ROWS_CASE(7) Q8_ROWS_CASE(8)
+        Q8_ROWS_CASE(9) Q8_ROWS_CASE(10) Q8_ROWS_CASE(11) Q8_ROWS_CASE(12)
+        Q8_ROWS_CASE(13) Q8_ROWS_CASE(14) Q8_ROWS_CASE(15) Q8_ROWS_CASE(16)
+#undef Q8_ROWS_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int S, bool PARTIALS, bool WST>
 hipError_t launch_s(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                     float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
@@ -237,6 +367,10 @@ hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, cons
                          float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
     if (matvec_batch_fits(M, K))  // several rows: read the weights once for all of them
         return launch_matvec_batch(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
+    if (!ws_t && K <= kMaxSteps * kStepBytes) {
+        if (P != nullptr) return launch_rows_any<true>(A, AS, W, WS, C, P, M, N, K, stream);
+        return launch_rows_any<false>(A, AS, W, WS, C, P, M, N, K, stream);
+    }
     if (P != nullptr) return launch_any<true, false>(A, AS, W, WS, C, P, M, N, K, stream);
     if (ws_t) return launch_any<false, true>(A, AS, W, WS, C, P, M, N, K, stream);
     return launch_any<false, false>(A, AS, W, WS, C, P, M, N, K, stream);

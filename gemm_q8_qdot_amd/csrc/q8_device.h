@@ -108,6 +108,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ v4i buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// Streaming form for data read once: cache policy bit 1 (nt).
+__device__ __forceinline__ v4i buffer_load16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
 __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }

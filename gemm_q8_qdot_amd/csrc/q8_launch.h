@@ -51,4 +51,8 @@ hipError_t launch_quantize(const float* X, int8_t* Q, float* D, int rows, int K,
 // call stays safe inside a captured graph).
 hipError_t launch_fill_zero(float* C, int64_t count, hipStream_t stream);
 
+// Compute units of the current device (queried once per device; 256 on
+// MI355X).  Launch shapes that place one workgroup per compute unit use it.
+int device_cu_count();
+
 }  // namespace q8

@@ -1,4 +1,5 @@
-// Q8_0 quantization of f32 rows on the GPU, and a small fill kernel.
+// Q8_0 quantization of f32 rows on the GPU, a small fill kernel, and the
+// cached compute-unit count that launch shapes use.
 //
 // Format: "Quantized built-ins and formats", section "Q8_0" -- signed bytes,
 // one f32 scale per 32 consecutive values; activations use the same form
@@ -12,6 +13,8 @@
 // Layout of the work: 8 lanes per 32-value block, 4 values (16 bytes) per
 // lane, so one wave reads 1 KiB of contiguous f32 and writes 256 contiguous
 // bytes of Q.  HBM-bound: 4 bytes in, 1 + 1/8 bytes out per value.
+#include <atomic>
+
 #include "q8_device.h"
 #include "q8_launch.h"
 
@@ -81,6 +84,19 @@ hipError_t launch_fill_zero(float* C, int64_t count, hipStream_t stream) {
     const int64_t cap = 256 * 16;
     fill_zero_kernel<<<(unsigned)(need < cap ? need : cap), 256, 0, stream>>>(C, count);
     return hipGetLastError();
+}
+
+int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];  // zero until queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace q8

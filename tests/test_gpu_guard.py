@@ -1,0 +1,136 @@
+"""GPU: every kernel writes exactly its output, nothing around it.
+
+Each case places the output (C f32, or P int32) inside a larger buffer whose
+surrounding words hold a sentinel bit pattern, calls the C-ABI entry with
+the interior address, and checks that (a) the words before and after are
+untouched, (b) every output word was written, and (c) the output matches
+the oracle (partials bit for bit, f32 within the contraction's tolerance).
+The shapes reach every kernel the library dispatches to (``q8_qdot_path``
+and the Q5_0 / transposed-scale entries), each with ragged extents.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import gemm_q8_qdot_amd as q8
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096            # sentinel words on each side of the output
+SENTINEL = 0x7FC0DEAD   # a NaN payload no kernel produces as f32, and an unlikely int32
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible gfx950 GPU"
+    q8.ensure_built()
+    q8.load()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _guarded(n, dtype, dev):
+    buf = torch.full((GUARD + n + GUARD,), SENTINEL, dtype=torch.int32, device=dev)
+    return buf, buf[GUARD:GUARD + n].view(dtype)
+
+
+def _check_guard(buf, n, what):
+    host = buf.cpu().numpy()
+    before, inner, after = host[:GUARD], host[GUARD:GUARD + n], host[GUARD + n:]
+    assert (before == SENTINEL).all(), "%s: wrote %d words before the output" % (what, (before != SENTINEL).sum())
+    assert (after == SENTINEL).all(), "%s: wrote %d words after the output" % (what, (after != SENTINEL).sum())
+    unwritten = int((inner == SENTINEL).sum())
+    assert unwritten == 0, "%s: %d output words never written" % (what, unwritten)
+
+
+def _t(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+# (entry, M, N, K): the kernel each shape reaches is in the comment.
+CASES = [
+    ("qdot", 1, 5000, 4096),      # one-row decode kernel, rows per wave ragged
+    ("qdot", 1, 3000, 9248),      # one-row decode kernel, prefetching form
+    ("qdot", 1, 130, 16416),      # chunked matvec (rows longer than 16 KiB)
+    ("qdot", 3, 1000, 4128),      # small-batch matvec
+    ("qdot", 70, 300, 1056),      # K-split MFMA GEMM
+    ("qdot", 129, 14336, 96),     # LDS-staged MFMA GEMM, ragged M
+    ("qmma", 1, 1000, 4096),      # matvec with transposed scales
+    ("qmma", 5, 1000, 2080),      # small batch with transposed scales
+    ("qmma", 130, 14300, 128),    # staged GEMM with transposed scales
+    ("q50", 1, 1001, 4096),       # Q5_0 matvec
+    ("q50", 9, 100, 1056),        # Q5_0 K-split GEMM
+    ("q50t", 2, 333, 2048),       # Q5_0 matvec, transposed scales
+]
+
+
+@pytest.mark.parametrize("entry,M,N,K", CASES)
+def test_output_bounds(dev, entry, M, N, K):
+    _say("[guard] %s M=%d N=%d K=%d" % (entry, M, N, K))
+    KB = K // 32
+    seed = M * 131 + N * 7 + K
+    A = synth.random_i8((M, K), seed)
+    AS = synth.random_scales((M, KB), seed + 1, 1e-3, 1.0)
+    WS = synth.random_scales((N, KB), seed + 2, 1e-3, 1.0)
+    q50 = entry.startswith("q50")
+    ws_t = entry in ("qmma", "q50t")
+    W = synth.random_q50(N, K, seed + 3) if q50 else synth.random_i8((N, K), seed + 3)
+    WSx = np.ascontiguousarray(WS.T) if ws_t else WS
+    tA, tAS, tW, tWS = _t(A, dev), _t(AS, dev), _t(W, dev), _t(WSx, dev)
+
+    cbuf, C = _guarded(M * N, torch.float32, dev)
+    C = C.view(M, N)
+    if entry == "qdot":
+        q8.q8_qdot(tA, tAS, tW, tWS, C)
+    elif entry == "qmma":
+        q8.q8_qmma(tA, tAS, tW, tWS, C)
+    elif entry == "q50":
+        q8.q8_q50_qdot(tA, tAS, tW, tWS, C)
+    else:
+        q8.q8_q50_qmma(tA, tAS, tW, tWS, C)
+    pbuf, P = _guarded(M * N * KB, torch.int32, dev)
+    P = P.view(M, N, KB)
+    if q50:
+        q8.q8_q50_partials(tA, tW, P)
+    else:
+        q8.q8_qdot_partials(tA, tW, P)
+    torch.cuda.synchronize()
+    _check_guard(cbuf, M * N, entry + " C")
+    _check_guard(pbuf, M * N * KB, entry + " P")
+
+    if q50:
+        Pref = oracle.q50_block_partials(A, W)
+        out, mag = (oracle.q50_qmma_f64 if ws_t else oracle.q50_qdot_f64)(A, AS, W, WSx)
+    else:
+        Pref = oracle.block_partials(A, W)
+        out, mag = (oracle.qmma_f64 if ws_t else oracle.qdot_f64)(A, AS, W, WSx)
+    assert np.array_equal(P.cpu().numpy(), Pref)
+    assert oracle.within_tolerance(C.cpu().numpy(), out, mag).all()
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (3, 4128), (257, 1056)])
+def test_quantize_bounds(dev, rows, K):
+    # The quantizer clamps codes to [-127, 127], so -128 marks unwritten bytes.
+    _say("[guard] quantize rows=%d K=%d" % (rows, K))
+    X = synth.random_f32((rows, K), rows * 7 + K)
+    qbuf = torch.full((GUARD + rows * K + GUARD,), -128, dtype=torch.int8, device=dev)
+    Q = qbuf[GUARD:GUARD + rows * K].view(rows, K)
+    dbuf, D = _guarded(rows * (K // 32), torch.float32, dev)
+    D = D.view(rows, K // 32)
+    q8.q8_quantize(_t(X, dev), Q, D)
+    torch.cuda.synchronize()
+    host = qbuf.cpu().numpy()
+    assert (host[:GUARD] == -128).all() and (host[GUARD + rows * K:] == -128).all()
+    assert not (host[GUARD:GUARD + rows * K] == -128).any()
+    _check_guard(dbuf, rows * (K // 32), "quantize D")
+    Qref, Dref = oracle.quantize_rows(X)
+    assert np.array_equal(Q.cpu().numpy(), Qref)
+    assert np.array_equal(D.cpu().numpy().view(np.uint32), Dref.view(np.uint32))

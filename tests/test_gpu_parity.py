@@ -134,6 +134,24 @@ EDGE = [
     (12, 70, 16416), (4, 4099, 14336), (9, 1, 14336), (127, 300, 4160), (40, 2050, 8224),
 ]
 
+# One activation row with K <= 16 KiB (the decode kernel, launched as one
+# workgroup per compute unit with a grid stride over weight rows): rows per
+# wave that do not divide evenly, the prefetching form for rows of 9..14 KiB
+# with an odd and an even number of rows per wave, rows of 15 and 16 KiB,
+# and K that is not a multiple of 1 KiB.
+ROWS = [(1, 5000, 4096), (1, 3000, 9248), (1, 1025, 14336), (1, 2049, 16384), (1, 7, 15360),
+        (1, 2048 * 3 + 5, 1056), (1, 100, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", ROWS)
+def test_decode_rows(dev, M, N, K):
+    seed = N * 17 + K
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 10.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-4, 1.0)
+    _check_full(A, AS, W, WS, dev, "rows")
+
 
 # Small decode batches (2..7 activation rows): one weight pass for all rows,
 # at the decode workloads' sizes and at ragged ones.
