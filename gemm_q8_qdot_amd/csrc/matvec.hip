@@ -204,14 +204,21 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 // the current row is computed (PF).  Fewer bytes in flight per compute unit
 // than either made the stream slower; more (more waves, or several
 // workgroups per compute unit) made it slower too.
-template <int S, bool PF, bool PARTIALS, int T>
+// WST: weight scales stored transposed, [K/32][N] (qmma_t), staged through
+// LDS per tile of rows (see below).
+template <int S, bool PF, bool PARTIALS, bool WST, int T>
 __global__ void __launch_bounds__(T)
 matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                    const int8_t* __restrict__ W, const float* __restrict__ WS,
                    float* __restrict__ C, int32_t* __restrict__ P, int N, int K) {
     const int lane = threadIdx.x & (kWave - 1);
+    const int nwg = gridDim.x;
+    // With WST, the workgroups of one XCD (workgroup b runs on XCD b mod 8)
+    // take neighbouring row shares, so the scale lines they share stay in
+    // that XCD's L2.
+    const int wgx = (WST && nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : (int)blockIdx.x;
     // wave-uniform (readfirstlane), so the row resources live in SGPRs
-    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (T / kWave) + (int)(threadIdx.x / kWave));
+    const int wave = __builtin_amdgcn_readfirstlane(wgx * (T / kWave) + (int)(threadIdx.x / kWave));
     const int nwaves = gridDim.x * (T / kWave);
     const int i = blockIdx.y;
     const int KB = K / kBlock;
@@ -240,7 +247,7 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         for (int s = 0; s < S; ++s) {
             const int off = s * kStepBytes + lo;
             w[s] = buffer_load16_nt(rW, off < K ? off : kNoRead, 0);  // read once: streaming
-            if constexpr (!PARTIALS) ws[s] = buffer_load_f32(rWS, off < K ? (off / kBlock) * 4 : kNoRead, 0);
+            if constexpr (!PARTIALS && !WST) ws[s] = buffer_load_f32(rWS, off < K ? (off / kBlock) * 4 : kNoRead, 0);
         }
     };
     auto compute_row = [&](int j, const v4i (&w)[S], const float (&ws)[S]) {
@@ -262,7 +269,78 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         }
     };
 
-    if constexpr (PF) {
+    if constexpr (WST) {
+        // Workgroup wgx owns the rows [r_lo, r_hi) (a contiguous share) and
+        // takes them in tiles of up to kTile rows: the tile's scales of every
+        // block are staged through LDS ([row][block], padded against bank
+        // conflicts) by the whole workgroup from runs of WST that are
+        // contiguous in the row index, then its waves take the tile's rows
+        // in turn with no further barrier.  Every wave of the workgroup runs
+        // the same tiles (the staging uses barriers).
+        constexpr int kRowsWG = T / kWave;
+        constexpr int kKBMax = S * (kStepBytes / kBlock);
+        constexpr int kPitch = kKBMax + 1;
+        constexpr int kTile0 = 8192 / kKBMax;  // ~32 KiB of scales per tile
+        constexpr int kTile = kTile0 < kRowsWG ? kRowsWG : (kTile0 > 64 ? 64 : kTile0 / kRowsWG * kRowsWG);
+        constexpr int kStagePer = (kTile * kKBMax + T - 1) / T;
+        __shared__ float ws_tile[kTile * kPitch];
+        const __amdgpu_buffer_rsrc_t rWST = buffer_rsrc(WS, (int64_t)KB * N * 4);
+        const int wv = (int)(threadIdx.x / kWave);
+        const int r_lo = (int)((int64_t)N * wgx / nwg);
+        const int r_hi = (int)((int64_t)N * (wgx + 1) / nwg);
+        float ws[S];
+        for (int t0 = r_lo; t0 < r_hi; t0 += kTile) {
+            const int t1 = t0 + kTile < r_hi ? t0 + kTile : r_hi;
+            int j = t0 + wv;
+            // this wave's first rows of the tile are in flight during the staging
+            v4i w0[S], w1[S];
+            if (j < t1) load_row(j, w0, ws);
+            if constexpr (S <= 12)
+                if (j + kRowsWG < t1) load_row(j + kRowsWG, w1, ws);
+            float st[kStagePer];
+#pragma unroll
+            for (int u = 0; u < kStagePer; ++u) {
+                // consecutive threads: consecutive rows of one block
+                const int idx = threadIdx.x + u * T;
+                const int b = idx / kTile, r = idx % kTile;
+                st[u] = buffer_load_f32(rWST, (b < KB && t0 + r < t1) ? (b * N + t0 + r) * 4 : kNoRead, 0);
+            }
+            // the previous tile's reads of ws_tile are done (no wait on loads)
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+            for (int u = 0; u < kStagePer; ++u) {
+                const int idx = threadIdx.x + u * T;
+                const int b = idx / kTile, r = idx % kTile;
+                if (b < kKBMax) ws_tile[r * kPitch + b] = st[u];
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            auto tile_ws = [&](int jj) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) ws[s] = ws_tile[(jj - t0) * kPitch + (s * kStepBytes + lo) / kBlock];
+            };
+            if constexpr (S <= 12) {
+                // two rows in flight: each row's compute is followed by the
+                // load of the row two steps ahead into its registers
+                while (j < t1) {
+                    const int j1 = j + kRowsWG;
+                    tile_ws(j);
+                    compute_row(j, w0, ws);
+                    if (j1 + kRowsWG < t1) load_row(j1 + kRowsWG, w0, ws);
+                    if (j1 >= t1) break;
+                    tile_ws(j1);
+                    compute_row(j1, w1, ws);
+                    if (j1 + 2 * kRowsWG < t1) load_row(j1 + 2 * kRowsWG, w1, ws);
+                    j = j1 + kRowsWG;
+                }
+            } else {
+                for (; j < t1; j += kRowsWG) {
+                    if (j != t0 + wv) load_row(j, w0, ws);
+                    tile_ws(j);
+                    compute_row(j, w0, ws);
+                }
+            }
+        }
+    } else if constexpr (PF) {
         // Two rows in flight: ping-pong registers, loop unrolled by two.
         v4i w0[S], w1[S];
         float ws0[S], ws1[S];
@@ -288,26 +366,26 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     }
 }
 
-template <int S, bool PARTIALS>
+template <int S, bool PARTIALS, bool WST>
 hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     // Prefetch for rows of 9..14 KiB (two rows of 15 or 16 KiB in registers
     // would spill).
-    constexpr bool kPF = S > 8 && S <= 14;
+    constexpr bool kPF = !WST && S > 8 && S <= 14;
     constexpr int kT = kPF ? 256 : 512;
     const int cap = device_cu_count() * (kT / kWave);
     const int waves = N < cap ? N : cap;
     const int wgs = (waves + kT / kWave - 1) / (kT / kWave);
-    matvec_rows_kernel<S, kPF, PARTIALS, kT><<<dim3(wgs, M), kT, 0, stream>>>(A, AS, W, WS, C, P, N, K);
+    matvec_rows_kernel<S, kPF, PARTIALS, WST, kT><<<dim3(wgs, M), kT, 0, stream>>>(A, AS, W, WS, C, P, N, K);
     return hipGetLastError();
 }
 
-template <bool PARTIALS>
+template <bool PARTIALS, bool WST>
 hipError_t launch_rows_any(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                            float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     switch ((K + kStepBytes - 1) / kStepBytes) {
 #define Q8_ROWS_CASE(S_) \
-    case S_: return launch_rows<S_, PARTIALS>(A, AS, W, WS, C, P, M, N, K, stream);
+    case S_: return launch_rows<S_, PARTIALS, WST>(A, AS, W, WS, C, P, M, N, K, stream);
         Q8_ROWS_CASE(1) Q8_ROWS_CASE(2) Q8_ROWS_CASE(3) Q8_ROWS_CASE(4)
         Q8_ROWS_CASE(5) Q8_ROWS_CASE(6) Q8_ROWS_CASE(7) Q8_ROWS_CASE(8)
         Q8_ROWS_CASE(9) Q8_ROWS_CASE(10) Q8_ROWS_CASE(11) Q8_ROWS_CASE(12)
@@ -367,9 +445,12 @@ hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, cons
                          float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
     if (matvec_batch_fits(M, K))  // several rows: read the weights once for all of them
         return launch_matvec_batch(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
-    if (!ws_t && K <= kMaxSteps * kStepBytes) {
-        if (P != nullptr) return launch_rows_any<true>(A, AS, W, WS, C, P, M, N, K, stream);
-        return launch_rows_any<false>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (K <= kMaxSteps * kStepBytes) {
+        if (P != nullptr) return launch_rows_any<true, false>(A, AS, W, WS, C, P, M, N, K, stream);
+        // transposed scales: the column's offsets must fit the 32-bit buffer range
+        if (!ws_t) return launch_rows_any<false, false>(A, AS, W, WS, C, P, M, N, K, stream);
+        if ((int64_t)(K / kBlock) * N * 4 < INT32_MAX)
+            return launch_rows_any<false, true>(A, AS, W, WS, C, P, M, N, K, stream);
     }
     if (P != nullptr) return launch_any<true, false>(A, AS, W, WS, C, P, M, N, K, stream);
     if (ws_t) return launch_any<false, true>(A, AS, W, WS, C, P, M, N, K, stream);

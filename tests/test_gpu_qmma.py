@@ -110,6 +110,11 @@ def test_workload_prompt_size_sampled(dev):
 
 SHAPES = [
     (1, 37, 1056), (3, 129, 2080), (7, 300, 1024), (5, 64, 4096),      # matvec
+    # one row: shares of rows per workgroup that are ragged, several
+    # LDS tiles per share, a single row, the two-rows-in-flight form and
+    # the one-row form (rows over 12 KiB), rows longer than 16 KiB
+    (1, 14300, 4096), (1, 40000, 2048), (1, 1, 64), (1, 3000, 12288), (1, 1000, 13312),
+    (1, 2049, 16384), (1, 100, 16416),
     (9, 37, 96), (33, 100, 4096), (127, 300, 4160), (64, 4099, 128),    # K-split
     (512, 7168, 1024),                                                  # staged, 16-byte scales
     (512, 7170, 1024), (256, 14400, 4128), (136, 14300, 160),           # staged, dword scales
@@ -122,7 +127,7 @@ def test_shapes(dev, M, N, K):
     _check(A, AS, W, WST, dev, "shape")
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 7168, 1024), (64, 4096, 512), (2, 100, 256)])
+@pytest.mark.parametrize("M,N,K", [(512, 7168, 1024), (64, 4096, 512), (2, 100, 256), (1, 1000, 4096)])
 def test_misaligned_scales(dev, M, N, K):
     A, AS, W, WST = _random_case(M, N, K, 55 + M)
     _check(A, AS, W, WST, dev, "misaligned", misalign=True)
