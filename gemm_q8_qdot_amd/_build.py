@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libq8qdot.so")
 
-SOURCES = ("q8qdot_api.hip", "matvec.hip", "matvec_batch.hip", "matvec_q50.hip", "qgemm.hip",
+SOURCES = ("q8qdot_api.hip", "matvec.hip", "matvec_q50.hip", "qgemm.hip",
            "qgemm_ksplit.hip", "quantize.hip")
 ARCH = "gfx950"
 

@@ -1,5 +1,4 @@
 // Q8_0 matvec for small M (decode step): C[i, :] = qdot_t(A[i, :], AS[i, :], W, WS).
-// (Batches of 2..7 rows with K <= 16 KiB go to matvec_batch.hip.)
 //
 // What is computed: the qdot_t row of the Q8_0 table ("Phobos Language Spec",
 // section "Quantized built-ins"), with the inner block sum in integers as the
@@ -12,21 +11,21 @@
 // against 64 output columns per CTA, Q8_0 section) and lanes_matvec (one warp
 // per row, lane-strided 4-element runs, a lane fold; "Uniform, warp-uniform
 // and varying").  Design here, for CDNA4 wave64:
-//   - a wave owns R weight rows at a time and walks rows with a grid stride;
+//   - a wave walks weight rows with a grid stride;
 //   - lane l reads bytes [1024 s + 16 l, +16) of a row: each load instruction
 //     covers 1 KiB of contiguous weight bytes, so W streams fully coalesced;
 //   - lanes 2m and 2m+1 hold the two halves of block (1024 s)/32 + m: each
 //     lane does 4 v_dot4_i32_i8, one DPP swap adds the partner's half, giving
-//     the exact int32 block sum in both lanes;
-//   - the activation row and its scales stay in VGPRs for the whole kernel
-//     when K <= 16 KiB (else they are re-read per chunk); the activation scale
-//     is zeroed in odd lanes so each block is scaled and accumulated once;
+//     the exact int32 block sum in both lanes; only the even lane scales and
+//     accumulates it;
 //   - the f32 accumulator is folded across the wave with DPP (no LDS).
-// Two kernels share this scheme: matvec_rows_kernel (one activation row,
-// K <= 16 KiB, weight scales [N][K/32]: the decode case, with row-sized
-// buffer resources and a launch of one workgroup per compute unit) and
-// matvec_kernel (transposed weight scales, which it stages through LDS per
-// workgroup, and rows longer than 16 KiB, taken in 16 KiB chunks).
+// Two kernels share this scheme.  matvec_rows_kernel (K <= 16 KiB): one
+// activation row held in VGPRs, or a batch of 2..7 rows staged once in LDS
+// so that the weights are read once for all of them; row-sized buffer
+// resources; one or two workgroups per compute unit.  matvec_kernel (rows
+// longer than 16 KiB): one activation row per grid row, taken in 16 KiB
+// chunks.  Either takes the weight scales as [N][K/32] or transposed
+// ([K/32][N], the qmma_t form), which are staged through LDS.
 // HBM-bound: algorithmic traffic is N*K weight bytes + N*K/8 scale bytes.
 #include "q8_device.h"
 #include "q8_launch.h"
@@ -192,25 +191,46 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     }
 }
 
-// ---- One activation row, K <= 16 KiB: the main decode kernel.
-// A wave holds its lanes' slice of the activation row (and scales) in VGPRs
-// and walks weight rows with a grid stride.  Each row is read through a
+// ---- K <= 16 KiB: the decode kernel (one activation row, or a small batch).
+// A wave walks weight rows with a grid stride.  Each row is read through a
 // buffer resource built for that row alone (its base is wave-uniform, so the
 // resource sits in SGPRs): a lane's offset past K, or a row past N, reads
 // zero, so there are no lane masks and no 64-bit address arithmetic, and the
-// whole wave fits in few VGPRs.  Launch shape, measured on MI355X: rows of up
-// to 8 KiB run one 8-wave workgroup per compute unit; longer rows run one
-// 4-wave workgroup per compute unit with the next row's loads issued before
-// the current row is computed (PF).  Fewer bytes in flight per compute unit
-// than either made the stream slower; more (more waves, or several
-// workgroups per compute unit) made it slower too.
+// whole wave fits in few VGPRs.  One activation row (MULTI false, the row is
+// blockIdx.y): the lane's slice of it and of its scales stays in VGPRs.
+// Several rows (MULTI, 2 <= M <= 7): the workgroup stages all of them and
+// their scales in LDS once, and every 16-byte weight piece is dotted with
+// the M activation pieces read back from LDS, so the weights cross the bus
+// once for all rows.  Launch shape, measured on MI355X: rows of up to 8 KiB
+// run one 8-wave workgroup per compute unit; longer rows run one 4-wave
+// workgroup per compute unit with the next row's loads issued before the
+// current row is computed (PF).  Fewer bytes in flight per compute unit than
+// either made the stream slower; more (more waves, or several workgroups per
+// compute unit) made it slower too.
 // WST: weight scales stored transposed, [K/32][N] (qmma_t), staged through
 // LDS per tile of rows (see below).
-template <int S, bool PF, bool PARTIALS, bool WST, int T>
+constexpr int kMaxBatch = 7;
+// Rows per LDS tile of transposed scales (~32 KiB of scales, a whole number
+// of rows per wave, at most 64), and that tile's static LDS bytes.
+constexpr int wst_tile_rows(int S, int T) {
+    const int rows_wg = T / kWave, kb = S * (kStepBytes / kBlock), t0 = 8192 / kb;
+    return t0 < rows_wg ? rows_wg : (t0 > 64 ? 64 : t0 / rows_wg * rows_wg);
+}
+constexpr size_t wst_tile_bytes(int S, int T) { return (size_t)wst_tile_rows(S, T) * (S * (kStepBytes / kBlock) + 1) * 4; }
+// LDS of a staged batch of M rows (S KiB each): the rows at a pitch of S
+// KiB, then their scales at a pitch of S * 32 + 64 floats (whole 256-byte
+// loads).
+template <int S>
+constexpr size_t batch_smem_bytes(int M, bool partials) {
+    return (size_t)M * S * kStepBytes + (partials ? 0 : (size_t)M * (S * (kStepBytes / kBlock) + 64) * 4);
+}
+
+template <int S, bool PF, bool PARTIALS, bool WST, bool MULTI, int T>
 __global__ void __launch_bounds__(T)
 matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                    const int8_t* __restrict__ W, const float* __restrict__ WS,
-                   float* __restrict__ C, int32_t* __restrict__ P, int N, int K) {
+                   float* __restrict__ C, int32_t* __restrict__ P, int M, int N, int K) {
+    extern __shared__ __align__(16) int8_t rows_smem[];
     const int lane = threadIdx.x & (kWave - 1);
     const int nwg = gridDim.x;
     // With WST, the workgroups of one XCD (workgroup b runs on XCD b mod 8)
@@ -220,52 +240,102 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     // wave-uniform (readfirstlane), so the row resources live in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(wgx * (T / kWave) + (int)(threadIdx.x / kWave));
     const int nwaves = gridDim.x * (T / kWave);
-    const int i = blockIdx.y;
+    const int i = MULTI ? 0 : (int)blockIdx.y;
     const int KB = K / kBlock;
     const bool even = (lane & 1) == 0;
     const int lo = lane * 16;
+    // MULTI: [M][S KiB] activation bytes, then [M][S * 32] f32 scales
+    constexpr int kBatchPitch = S * kStepBytes;
+    constexpr int kBatchSPitch = S * (kStepBytes / kBlock) + 64;  // whole 256-byte loads
+    int8_t* a_lds = rows_smem;
+    float* as_lds = reinterpret_cast<float*>(rows_smem + M * kBatchPitch);
 
-    // This lane's activation bytes [1024 s + 16 lane, +16) and, in even
-    // lanes, the scale of their block (odd lanes hold 0: each block's
+    // One row: this lane's activation bytes [1024 s + 16 lane, +16) and, in
+    // even lanes, the scale of their block (odd lanes hold 0: each block's
     // product is accumulated once).
-    const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A + (int64_t)i * K, K);
-    const __amdgpu_buffer_rsrc_t rAS = buffer_rsrc(AS + (int64_t)i * KB, (int64_t)KB * 4);
-    v4i a[S];
-    float as[S];
+    v4i a[MULTI ? 1 : S];
+    float as[MULTI ? 1 : S];
+    // (Offsets past the row's K bytes or K/32 scales read zero through the
+    // buffer range check.)
+    if constexpr (!MULTI) {
+        const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A + (int64_t)i * K, K);
+        const __amdgpu_buffer_rsrc_t rAS = buffer_rsrc(AS + (int64_t)i * KB, (int64_t)KB * 4);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int off = s * kStepBytes + lo;
-        a[s] = buffer_load16(rA, off < K ? off : kNoRead, 0);
-        if constexpr (!PARTIALS)
-            as[s] = buffer_load_f32(rAS, (even && off < K) ? (off / kBlock) * 4 : kNoRead, 0);
+        for (int s = 0; s < S; ++s) {
+            a[s] = buffer_load16(rA, lo + s * kStepBytes, 0);
+            if constexpr (!PARTIALS) {
+                const float v = buffer_load_f32(rAS, (lo / kBlock) * 4 + s * kStepBytes / kBlock * 4, 0);
+                as[s] = even ? v : 0.0f;
+            }
+        }
     }
+    // Several rows: stage them (and their scales) in LDS with direct
+    // global -> LDS loads (no VGPRs), 1 KiB (scales: 256 bytes) per wave
+    // instruction, each row at a fixed pitch of S KiB (scales: S * 32
+    // floats) so that every LDS read below is one base address plus a
+    // constant; a row's bytes past K (scales past K/32) land as zeros.
+    // Callers issue their first weight row before this, so it is in flight
+    // meanwhile.
+    auto stage_batch = [&]() {
+        if constexpr (MULTI) {
+            const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+            const uint32_t a_base = lds_addr(a_lds);
+            for (int c = wv; c < M * S; c += T / kWave) {
+                const int m = c / S, piece = c % S;
+                const v4i dA = make_desc(A + (int64_t)m * K, K);
+                dma16(dA, a_base + m * kBatchPitch + piece * kStepBytes, lo + piece * kStepBytes, 0);
+            }
+            if constexpr (!PARTIALS) {
+                constexpr int kSPieces = (S * kStepBytes / kBlock * 4 + kWave * 4 - 1) / (kWave * 4);
+                const uint32_t s_base = lds_addr(as_lds);
+                for (int c = wv; c < M * kSPieces; c += T / kWave) {
+                    const int m = c / kSPieces, piece = c % kSPieces;
+                    const v4i dAS = make_desc(AS + (int64_t)m * KB, (int64_t)KB * 4);
+                    dma4(dAS, s_base + m * kBatchSPitch * 4 + piece * kWave * 4, (piece * kWave + lane) * 4, 0);
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    };
 
     auto load_row = [&](int j, v4i (&w)[S], float (&ws)[S]) {
         const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(W + (int64_t)j * K, K);
         const __amdgpu_buffer_rsrc_t rWS = buffer_rsrc(WS + (int64_t)j * KB, (int64_t)KB * 4);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            const int off = s * kStepBytes + lo;
-            w[s] = buffer_load16_nt(rW, off < K ? off : kNoRead, 0);  // read once: streaming
-            if constexpr (!PARTIALS && !WST) ws[s] = buffer_load_f32(rWS, off < K ? (off / kBlock) * 4 : kNoRead, 0);
+            w[s] = buffer_load16_nt(rW, lo + s * kStepBytes, 0);  // read once: streaming
+            if constexpr (!PARTIALS && !WST)
+                ws[s] = buffer_load_f32(rWS, (lo / kBlock) * 4 + s * kStepBytes / kBlock * 4, 0);
         }
     };
     auto compute_row = [&](int j, const v4i (&w)[S], const float (&ws)[S]) {
-        float acc = 0.0f;
+        constexpr int kM = MULTI ? kMaxBatch : 1;
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            int p = dot16(a[s], w[s], 0);
-            p += dpp_i32<kDppSwapPairs>(p);  // exact block sum in both lanes of the pair
-            if constexpr (PARTIALS) {
+        for (int m = 0; m < kM; ++m) {
+            if (MULTI && m >= M) break;  // uniform
+            const int row = MULTI ? m : i;
+            int32_t* Prow = P + ((int64_t)row * N + j) * KB;  // (PARTIALS) this row's blocks
+            float acc = 0.0f;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
                 const int off = s * kStepBytes + lo;
-                if (even && off < K) P[((int64_t)i * N + j) * KB + off / kBlock] = p;
-            } else {
-                acc = fmaf(as[s] * ws[s], (float)p, acc);
+                const v4i am = MULTI ? *reinterpret_cast<const v4i*>(a_lds + m * kBatchPitch + s * kStepBytes + lo) : a[s];
+                int p = dot16(am, w[s], 0);
+                p += dpp_i32<kDppSwapPairs>(p);  // exact block sum in both lanes of the pair
+                if constexpr (PARTIALS) {
+                    if (even && off < K) Prow[s * (kStepBytes / kBlock) + lane / 2] = p;
+                } else {
+                    const float asm_ = MULTI ? (even ? as_lds[m * kBatchSPitch + (s * kStepBytes + lo) / kBlock] : 0.0f) : as[s];
+                    acc = fmaf(asm_ * ws[s], (float)p, acc);
+                }
             }
-        }
-        if constexpr (!PARTIALS) {
-            const float tot = wave_sum(acc);
-            if (lane == 0) C[(int64_t)i * N + j] = tot;
+            if constexpr (!PARTIALS) {
+                const float tot = wave_sum(acc);
+                if (lane == 0) C[(int64_t)row * N + j] = tot;
+            }
+            // one activation row's LDS reads at a time (else all M rows' pieces
+            // would be read ahead into VGPRs)
+            if constexpr (MULTI) asm volatile("" ::: "memory");
         }
     };
 
@@ -280,8 +350,7 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         constexpr int kRowsWG = T / kWave;
         constexpr int kKBMax = S * (kStepBytes / kBlock);
         constexpr int kPitch = kKBMax + 1;
-        constexpr int kTile0 = 8192 / kKBMax;  // ~32 KiB of scales per tile
-        constexpr int kTile = kTile0 < kRowsWG ? kRowsWG : (kTile0 > 64 ? 64 : kTile0 / kRowsWG * kRowsWG);
+        constexpr int kTile = wst_tile_rows(S, T);
         constexpr int kStagePer = (kTile * kKBMax + T - 1) / T;
         __shared__ float ws_tile[kTile * kPitch];
         const __amdgpu_buffer_rsrc_t rWST = buffer_rsrc(WS, (int64_t)KB * N * 4);
@@ -289,6 +358,7 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         const int r_lo = (int)((int64_t)N * wgx / nwg);
         const int r_hi = (int)((int64_t)N * (wgx + 1) / nwg);
         float ws[S];
+        stage_batch();
         for (int t0 = r_lo; t0 < r_hi; t0 += kTile) {
             const int t1 = t0 + kTile < r_hi ? t0 + kTile : r_hi;
             int j = t0 + wv;
@@ -346,6 +416,7 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         float ws0[S], ws1[S];
         int j = wave;
         if (j < N) load_row(j, w0, ws0);
+        stage_batch();
         while (j < N) {
             const int j1 = j + nwaves;
             if (j1 < N) load_row(j1, w1, ws1);
@@ -357,35 +428,57 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             j = j2;
         }
     } else {
+        v4i w[S];
+        float ws[S];
+        if (wave < N) load_row(wave, w, ws);
+        stage_batch();
         for (int j = wave; j < N; j += nwaves) {
-            v4i w[S];
-            float ws[S];
-            load_row(j, w, ws);
+            if (j != wave) load_row(j, w, ws);
             compute_row(j, w, ws);
         }
     }
 }
 
-template <int S, bool PARTIALS, bool WST>
+template <int S, bool PARTIALS, bool WST, bool MULTI>
 hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    // Prefetch for rows of 9..14 KiB (two rows of 15 or 16 KiB in registers
-    // would spill).
-    constexpr bool kPF = !WST && S > 8 && S <= 14;
+    // Launch shapes, measured on MI355X.  One row: rows of up to 8 KiB, one
+    // 8-wave workgroup per compute unit; rows of 9..14 KiB, one 4-wave
+    // workgroup with the next row prefetched (PF; two rows of 15 or 16 KiB
+    // in registers would spill).  A batch of rows (more work per weight
+    // byte, so more waves to hide it): 8-wave workgroups, two per compute
+    // unit when their LDS fits (one with transposed scales on rows over
+    // 4 KiB, whose tiles then split worse).
+    constexpr bool kPF = !WST && !MULTI && S > 8 && S <= 14;
     constexpr int kT = kPF ? 256 : 512;
-    const int cap = device_cu_count() * (kT / kWave);
+    int wpc = (MULTI && !(WST && S > 4)) ? 2 : 1;  // workgroups per compute unit
+    auto kern = matvec_rows_kernel<S, kPF, PARTIALS, WST, MULTI, kT>;
+    size_t smem = 0;
+    if constexpr (MULTI) {
+        smem = batch_smem_bytes<S>(M, PARTIALS);
+        static bool attr_set = false;  // (idempotent: a race only repeats the call)
+        if (!attr_set) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)batch_smem_bytes<S>(kMaxBatch, PARTIALS));
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+    }
+    if (MULTI && wpc > 1 && (smem + (WST ? wst_tile_bytes(S, kT) : 0)) * wpc > 160 * 1024) wpc = 1;
+    const int cap = device_cu_count() * wpc * (kT / kWave);
     const int waves = N < cap ? N : cap;
     const int wgs = (waves + kT / kWave - 1) / (kT / kWave);
-    matvec_rows_kernel<S, kPF, PARTIALS, WST, kT><<<dim3(wgs, M), kT, 0, stream>>>(A, AS, W, WS, C, P, N, K);
+    kern<<<dim3(wgs, MULTI ? 1 : M), kT, smem, stream>>>(A, AS, W, WS, C, P, M, N, K);
     return hipGetLastError();
 }
 
-template <bool PARTIALS, bool WST>
+template <bool PARTIALS, bool WST, bool MULTI>
 hipError_t launch_rows_any(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                            float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     switch ((K + kStepBytes - 1) / kStepBytes) {
 #define Q8_ROWS_CASE(S_) \
-    case S_: return launch_rows<S_, PARTIALS, WST>(A, AS, W, WS, C, P, M, N, K, stream);
+    case S_: return launch_rows<S_, PARTIALS, WST, MULTI>(A, AS, W, WS, C, P, M, N, K, stream);
         Q8_ROWS_CASE(1) Q8_ROWS_CASE(2) Q8_ROWS_CASE(3) Q8_ROWS_CASE(4)
         Q8_ROWS_CASE(5) Q8_ROWS_CASE(6) Q8_ROWS_CASE(7) Q8_ROWS_CASE(8)
         Q8_ROWS_CASE(9) Q8_ROWS_CASE(10) Q8_ROWS_CASE(11) Q8_ROWS_CASE(12)
@@ -393,6 +486,14 @@ hipError_t launch_rows_any(const int8_t* A, const float* AS, const int8_t* W, co
 #undef Q8_ROWS_CASE
         default: return hipErrorInvalidValue;
     }
+}
+
+template <bool MULTI>
+hipError_t launch_rows_mode(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                            float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
+    if (P != nullptr) return launch_rows_any<true, false, MULTI>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_rows_any<false, true, MULTI>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_rows_any<false, false, MULTI>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 template <int S, bool PARTIALS, bool WST>
@@ -443,14 +544,12 @@ hipError_t launch_any(const int8_t* A, const float* AS, const int8_t* W, const f
 
 hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                          float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
-    if (matvec_batch_fits(M, K))  // several rows: read the weights once for all of them
-        return launch_matvec_batch(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
-    if (K <= kMaxSteps * kStepBytes) {
-        if (P != nullptr) return launch_rows_any<true, false>(A, AS, W, WS, C, P, M, N, K, stream);
-        // transposed scales: the column's offsets must fit the 32-bit buffer range
-        if (!ws_t) return launch_rows_any<false, false>(A, AS, W, WS, C, P, M, N, K, stream);
-        if ((int64_t)(K / kBlock) * N * 4 < INT32_MAX)
-            return launch_rows_any<false, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    // K <= 16 KiB: the decode kernel, for one row or (2..7 rows) reading the
+    // weights once for all of them.  Transposed scales are addressed with
+    // 32-bit offsets over the whole [K/32][N] array.
+    if (K <= kMaxSteps * kStepBytes && (!ws_t || (int64_t)(K / kBlock) * N * 4 < INT32_MAX)) {
+        if (M == 1) return launch_rows_mode<false>(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
+        if (M <= kMaxBatch) return launch_rows_mode<true>(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
     }
     if (P != nullptr) return launch_any<true, false>(A, AS, W, WS, C, P, M, N, K, stream);
     if (ws_t) return launch_any<false, true>(A, AS, W, WS, C, P, M, N, K, stream);

@@ -116,6 +116,40 @@ __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int v
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// ---- Buffer loads straight into LDS (direct global -> LDS DMA).
+typedef __attribute__((address_space(3))) char lds_char;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 family)
+
+// Raw buffer descriptor (in SGPRs) for `bytes` bytes at `base`; reads whose
+// offset is past the range return 0 (and write 0 to LDS).
+__device__ __forceinline__ v4i make_desc(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+    v4i d;
+    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF));  // stride 0
+    d.z = __builtin_amdgcn_readfirstlane(n);
+    d.w = kRsrcWord3;
+    return d;
+}
+
+// Lane l's 16 (dma16) or 4 (dma4) bytes from offset voff + soff land at
+// LDS address lds + l * size.  Issued from inline assembly, so the compiler
+// neither waits on them nor counts them: the caller waits (s_waitcnt vmcnt)
+// before the data is read.  m0 carries the LDS address.
+__device__ __forceinline__ void dma16(v4i desc, uint32_t lds, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(v4i desc, uint32_t lds, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    // wave-uniform: m0 is a scalar register
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(const lds_char*)p);
+}
+
 // LDS tiles of 128-byte row segments (four Q8_0 blocks = eight 16-byte
 // chunks per row): row r holds its chunks permuted, logical chunk c at
 // physical chunk c ^ swz(r).  Sixteen consecutive rows read at the same

@@ -9,18 +9,13 @@
 
 namespace q8 {
 
-// M < 8: wave64 matvec, one activation row per grid row (blockIdx.y).
+// M < 8: wave64 matvec.  K <= 16 KiB: one kernel for one activation row or
+// (2 <= M <= 7) for all rows at once, every weight row read once; longer
+// rows: one activation row per grid row, taken in 16 KiB chunks.
 // P == nullptr -> f32 output C; otherwise int32 partials P, C unused.
 // ws_t: WS is stored transposed, [K/32][N] (the qmma_t form); else [N][K/32].
 hipError_t launch_matvec(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                          float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream);
-
-// 2 <= M <= 7 with K <= 16 KiB: the activation rows staged in LDS, every
-// weight row read once for all of them.  Same P and ws_t conventions.
-bool matvec_batch_fits(int M, int K);
-hipError_t launch_matvec_batch(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                               float* C, int32_t* P, int M, int N, int K, bool ws_t,
-                               hipStream_t stream);
 
 // M >= 8: int8-MFMA block GEMM.  Same P convention.
 // qgemm_variant: 1 = one workgroup per 32 x 32 tile with the contraction

@@ -52,7 +52,6 @@ namespace {
 
 // ---------------------------------------------------------------- staged
 
-typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kMWaves = 4;                      // along M: one 32-row strip per SIMD
 constexpr int kNGroups = 4;                     // along N: tiles {0,1} {2,3} {4,5} {6}
@@ -63,7 +62,6 @@ constexpr int kSB = 4;                          // Q8_0 blocks per stage
 constexpr int kSeg = kSB * kBlock;              // 128 bytes of a row per stage
 constexpr int kRowsPerLoad = kWave * 16 / kSeg; // one 16-byte-per-lane load: 8 rows
 constexpr int kRing = 3;                        // LDS stages; loads run two stages ahead
-constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit dwords (gfx9 family)
 constexpr int kWSRows = 256;  // weight-scale rows per block in LDS (BN padded to whole loads)
 
 template <int TN>
@@ -78,36 +76,6 @@ struct StagedStage {
 template <int TN>
 constexpr size_t staged_smem_bytes() {
     return sizeof(StagedStage<TN>) * kRing + 1024;  // + spare area for dummy loads
-}
-
-// Raw buffer descriptor (in SGPRs) for `bytes` bytes at `base`; reads whose
-// offset is past the range return 0.
-__device__ __forceinline__ v4i make_desc(const void* base, int64_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
-    v4i d;
-    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    d.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF));  // stride 0
-    d.z = __builtin_amdgcn_readfirstlane(n);
-    d.w = kRsrcWord3;
-    return d;
-}
-
-// Buffer loads straight into LDS (lane l's bytes land at lds + l * size).
-// Issued from inline assembly so that the only waits on them are the
-// explicit vmcnt waits of the stage ring below.  m0 carries the LDS address;
-// nothing else in this kernel keeps a value in m0.
-__device__ __forceinline__ void dma16(v4i desc, uint32_t lds, int voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory");
-}
-__device__ __forceinline__ void dma4(v4i desc, uint32_t lds, int voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    // wave-uniform: m0 is a scalar register
-    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(const lds_char*)p);
 }
 
 // Weight-scale modes (WSM):

@@ -156,7 +156,7 @@ def test_decode_rows(dev, M, N, K):
 # Small decode batches (2..7 activation rows): one weight pass for all rows,
 # at the decode workloads' sizes and at ragged ones.
 BATCH = [(2, 14336, 4096), (4, 4096, 14336), (7, 4096, 4096), (3, 1000, 16384), (5, 333, 1056),
-         (6, 2, 32)]
+         (6, 2, 32), (7, 300, 16384), (2, 5000, 9216), (4, 2049, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", BATCH)

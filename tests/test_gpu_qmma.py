@@ -115,6 +115,9 @@ SHAPES = [
     # the one-row form (rows over 12 KiB), rows longer than 16 KiB
     (1, 14300, 4096), (1, 40000, 2048), (1, 1, 64), (1, 3000, 12288), (1, 1000, 13312),
     (1, 2049, 16384), (1, 100, 16416),
+    # small batches: the largest LDS footprint (7 rows of 16 KiB and their
+    # scales beside the scale tile), several tiles per share, ragged shares
+    (7, 500, 16384), (4, 3000, 8192), (2, 14336, 4096), (6, 40000, 1024),
     (9, 37, 96), (33, 100, 4096), (127, 300, 4160), (64, 4099, 128),    # K-split
     (512, 7168, 1024),                                                  # staged, 16-byte scales
     (512, 7170, 1024), (256, 14400, 4128), (136, 14300, 160),           # staged, dword scales
