@@ -96,6 +96,31 @@ __device__ __forceinline__ float2 ws_pair(float ws) {
     return make_float2(hi, hi * -kBiasF);
 }
 
+// acc[R0 + k] += as(lane 16 (l / 16) + R0 + k) * u[R0 + k] for k < 8: one
+// v_fmac_f32 per element whose first factor comes through the DPP
+// row_newbcast control, i.e. from lane R0 + k of the lane's 16-lane row.  A
+// lane thus holds one scale per 16-lane row position instead of sixteen.
+// The leading s_nop covers the two wait states a DPP source needs after a
+// VALU write of it.
+template <int R0>
+__device__ __forceinline__ void fmac_rowbcast8(float (&acc)[16], float as, const float (&u)[16]) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %8, %9 row_newbcast:%17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %8, %10 row_newbcast:%18 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %8, %11 row_newbcast:%19 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %8, %12 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %13 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %8, %14 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %8, %15 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %8, %16 row_newbcast:%24 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[R0]), "+v"(acc[R0 + 1]), "+v"(acc[R0 + 2]), "+v"(acc[R0 + 3]),
+          "+v"(acc[R0 + 4]), "+v"(acc[R0 + 5]), "+v"(acc[R0 + 6]), "+v"(acc[R0 + 7])
+        : "v"(as), "v"(u[R0]), "v"(u[R0 + 1]), "v"(u[R0 + 2]), "v"(u[R0 + 3]), "v"(u[R0 + 4]),
+          "v"(u[R0 + 5]), "v"(u[R0 + 6]), "v"(u[R0 + 7]),
+          "n"(R0), "n"(R0 + 1), "n"(R0 + 2), "n"(R0 + 3), "n"(R0 + 4), "n"(R0 + 5), "n"(R0 + 6),
+          "n"(R0 + 7));
+}
+
 // ---- raw buffer loads (SGPR resource + 32-bit per-lane offset) ----
 // A load whose per-lane offset is at or past the resource's byte count
 // returns zeros; kNoRead is such an offset for every resource here.

@@ -26,18 +26,24 @@
 //     u   = fma(ws_hi, D, -ws_hi * 12582912)   = round(ws_hi * p)
 //     acc = fma(AS[i, b], u, acc)
 // The truncation changes each term by at most 3 ulp (3.6e-7 relative); the
-// int32 partials stay exact (the debug entry subtracts the bias in integer).
-// (ws_hi, -ws_hi * 12582912) pairs are prepared once per workgroup while
-// staging.  Requires |WS| < 2^100 so the bias product stays finite.
+// int32 partials stay exact (the debug entry stores the raw sums).  Each lane
+// forms its (ws_hi, -ws_hi * 12582912) pair from the weight scale of its
+// column.  The activation scale of a result register's row comes from one
+// VGPR per block: lane 16 q + n of a 16-lane row holds the scale of row
+// tile_row(n, half), and the accumulate is a v_fmac_f32 whose scale operand
+// is broadcast from lane r of the row (DPP row_newbcast).  Requires
+// |WS| < 2^100 so the bias product stays finite.
 //
 // Two kernels:
-//   staged  -- large M: an 8-wave workgroup (4 along M x 2 along N) owns a
-//              128 x (32 TN) output tile; A, W and both scale slices are
-//              staged through LDS four blocks (128 k) at a time in a 3-stage
-//              ring filled by direct global->LDS loads, each issued between
-//              the MFMA/epilogue work of an earlier stage.  One workgroup per
-//              CU; tiles are ordered so the workgroups sharing a W slab sit
-//              on one XCD.
+//   staged  -- large M: a 16-wave workgroup owns a 128 x 224 output tile
+//              (four 32-row strips x seven 32-column weight tiles); A, W and
+//              both scale slices are staged through LDS four blocks (128 k)
+//              at a time in a 3-stage ring filled by direct global->LDS
+//              loads, each issued between the math of an earlier stage.  Each
+//              wave software-pipelines its tiles: the MFMA of the next
+//              tile-block is issued before the epilogue of the current one.
+//              One workgroup per CU; tiles are ordered so the workgroups
+//              sharing a W slab sit on one XCD.
 //   (shapes with too few large tiles go to qgemm_ksplit.hip: one
 //              workgroup per 32 x 32 tile, the contraction split across its
 //              waves.)
@@ -69,7 +75,7 @@ struct StagedStage {
     static constexpr int BN = TN * kTile;
     int8_t a[kBM * kSeg];
     int8_t w[BN * kSeg];
-    float as[kSB][kBM];
+    float as[kBM][kSB];       // [row][block]
     float ws[kSB * kWSRows];  // [block][row] (dword loads) or [row][block] (16-byte loads)
 };
 
@@ -114,7 +120,7 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     //           activation-scale job 2 (wv - 12) + 1 for wv >= 12;  dword
     //           modes: activation-scale job 2 (wv - 12) + 1 for wv >= 12,
     //           then weight-scale job wv
-    // Activation-scale job e: block e / 2, rows 64 (e % 2) + lane (dword).
+    // Activation-scale job e: rows 16 e .. 16 e + 15, four blocks each (dword).
     // Weight-scale job e: mode 1: rows 64 e + lane, blocks 0..3; mode 3:
     // block e, rows 4 lane .. 4 lane + 3; modes 0, 2: block e / 4, rows
     // 64 (e % 4) + lane (dword).
@@ -172,6 +178,7 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const int voff_even = (lane / 8) * K + 16 * c_even;
     const int voff_odd = (lane / 8) * K + 16 * (c_even ^ 1);
     const int voff_scale = lane * KB * 4;
+    const int voff_ascale = (lane / 4) * KB * 4 + (lane % 4) * 4;
 
     // A job that a wave does not have (or one past the last stage) still
     // issues, with voffset kNoRead (reads nothing, writes zeros) into the
@@ -198,15 +205,15 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     // Scale jobs.  A block past K (last stage only) still writes its LDS
     // slot, with zeros, so the epilogue never reads a stale or uninitialised
     // scale; the debug entry has no scales and loads none.
-    // Activation-scale job e (block e / 2, rows 64 (e % 2) + lane) of stage st.
+    // Activation-scale job e of stage st: rows 16 e + lane / 4, block lane % 4
+    // (LDS [row][block]: lane l's dword lands at as[16 e][l]).
     auto job_as = [&](int st, int rs, int e, bool real) {
         StagedStage<TN>& sg = ring[rs];
         const int kb0 = st * kSB;
-        const int sblk = e / 2, h = e % 2;
         const bool to_slot = real && !PARTIALS;
-        const bool ok = to_slot && sblk < KB - kb0;
-        const int vo = ok ? voff_scale + h * kWave * KB * 4 + sblk * 4 : kNoRead;
-        dma4(dAS, lds_addr(to_slot ? (const void*)&sg.as[sblk][h * kWave] : (const void*)spare), vo, kb0 * 4);
+        const bool ok = to_slot && (lane % 4) < KB - kb0;
+        const int vo = ok ? voff_ascale + e * 16 * KB * 4 : kNoRead;
+        dma4(dAS, lds_addr(to_slot ? (const void*)&sg.as[16 * e][0] : (const void*)spare), vo, kb0 * 4);
     };
     // Weight-scale job e of stage st.
     auto job_ws = [&](int st, int rs, int e, bool real) {
@@ -265,6 +272,9 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 #pragma unroll
     for (int s = 0; s < kSB; ++s) frag_off[s] = col * kSeg + 16 * ((2 * s + half) ^ swz(col));
 
+    // Row of the activation-scale tile this lane holds for the DPP broadcast.
+    const int as_row = mw * kTile + tile_row(lane % 16, half);
+
     v16i bias;
 #pragma unroll
     for (int r = 0; r < 16; ++r) bias[r] = PARTIALS ? 0 : kBias;
@@ -277,48 +287,22 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-    // The math of block s of stage st: this wave's one or two tiles.
-    auto block_math = [&](auto nt_const, const StagedStage<TN>& sg, int st, int s) {
+    // Debug entry: the int32 block sums of block s of stage st for this
+    // wave's one or two tiles, stored raw (blocks past K are skipped).
+    auto block_partials = [&](auto nt_const, const StagedStage<TN>& sg, int st, int s) {
         constexpr int NT = decltype(nt_const)::value;
         const int kb = st * kSB + s;
         const v4i af = *reinterpret_cast<const v4i*>(sg.a + mw * kTile * kSeg + frag_off[s]);
-        if constexpr (PARTIALS) {
-            if (kb < KB) {
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (t0 + t) * kTile * kSeg + frag_off[s]);
-                    const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
-                    const int j = j0 + (t0 + t) * kTile + col;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = i0 + mw * kTile + tile_row(r, half);
-                        if (i < M && j < N) P[((int64_t)i * N + j) * KB + kb] = d[r];
-                    }
-                }
-            }
-        } else {
-            // Blocks past K (last stage only) read zero weight scales and
-            // add exactly 0, so there is no per-block branch here.
-            float asv[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&sg.as[s][mw * kTile + 8 * q + 4 * half]);
-                asv[4 * q + 0] = a4.x;
-                asv[4 * q + 1] = a4.y;
-                asv[4 * q + 2] = a4.z;
-                asv[4 * q + 3] = a4.w;
-            }
+        if (kb < KB) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (t0 + t) * kTile * kSeg + frag_off[s]);
                 const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
-                // the (ws_hi, bias product) pair of this lane's weight row
-                const int wrow = (t0 + t) * kTile + col;
-                const float2 wp = ws_pair(WS_ROWMAJOR ? sg.ws[wrow * kSB + s] : sg.ws[s * kWSRows + wrow]);
+                const int j = j0 + (t0 + t) * kTile + col;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
-                    acc[t][r] = fmaf(asv[r], u, acc[t][r]);
+                    const int i = i0 + mw * kTile + tile_row(r, half);
+                    if (i < M && j < N) P[((int64_t)i * N + j) * KB + kb] = d[r];
                 }
             }
         }
@@ -337,38 +321,117 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     wait_vmcnt_stage();
     __builtin_amdgcn_s_barrier();
 
+    // One tile-block's epilogue: acc[r] += AS[row r, b] * round(ws_hi * p[r])
+    // with p[r] read from the bias-seeded MFMA result (see the file head);
+    // the lane's activation scale is broadcast from lane r of its 16-lane row.
+    auto epilogue = [&](const v16i& d, float2 wp, float as_blk, float (&a)[16]) {
+        float u[16];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) u[r] = fmaf(wp.x, __int_as_float(d[r]), wp.y);
+        fmac_rowbcast8<0>(a, as_blk, u);
+#pragma unroll
+        for (int r = 8; r < 16; ++r) u[r] = fmaf(wp.x, __int_as_float(d[r]), wp.y);
+        fmac_rowbcast8<8>(a, as_blk, u);
+    };
+
     // The stage loop and the stores, for a wave with NT (1 or 2) tiles: one
     // straight run of code per case (a branch per tile inside the loop makes
     // the register allocator spill).
     auto run = [&](auto nt_const) {
         constexpr int NT = decltype(nt_const)::value;
         int rs = 0;  // ring slot of stage st; stage st + 2 goes to the slot before it
-        for (int st = 0; st < nstages; ++st) {
-            const bool ahead = st + 2 < nstages;
-            const int rs2 = rs == 0 ? kRing - 1 : rs - 1;
-            const StagedStage<TN>& sg = ring[rs];
-            // The loads of stage st + 2 (two ahead) go between this stage's blocks.
+        if constexpr (PARTIALS) {
+            for (int st = 0; st < nstages; ++st) {
+                const bool ahead = st + 2 < nstages;
+                const int rs2 = rs == 0 ? kRing - 1 : rs - 1;
+                const StagedStage<TN>& sg = ring[rs];
 #pragma unroll
-            for (int s = 0; s < kSB; ++s) {
-                fetch_slice(st + 2, rs2, s, ahead);
-                block_math(nt_const, sg, st, s);
-                // Pin the accumulators here: without it the compiler sinks
-                // the epilogues of all four blocks below the last MFMA and
-                // holds 16 VGPRs per pending MFMA result (spills).
-                if constexpr (!PARTIALS)
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; r += 4)
-                        asm volatile("" : "+v"(acc[t][r]), "+v"(acc[t][r + 1]), "+v"(acc[t][r + 2]),
-                                     "+v"(acc[t][r + 3]));
+                for (int s = 0; s < kSB; ++s) {
+                    fetch_slice(st + 2, rs2, s, ahead);
+                    block_partials(nt_const, sg, st, s);
+                }
+                wait_vmcnt_stage();
+                __builtin_amdgcn_s_barrier();
+                rs = rs == kRing - 1 ? 0 : rs + 1;
             }
-            wait_vmcnt_stage();
-            // Bare barrier (no fence): the loads of stage st + 2 stay in flight.
-            __builtin_amdgcn_s_barrier();
-            rs = rs == kRing - 1 ? 0 : rs + 1;
-        }
-        if constexpr (!PARTIALS) {
+        } else {
+            // Software pipeline over the stage's 4 NT tile-blocks q = NT s + t
+            // (block s, weight tile t): the MFMA of q is issued before the
+            // epilogue of q - 1, so every MFMA runs while the previous
+            // epilogue executes.  Results alternate between two register
+            // tiles (4 NT is even: tile-block q always uses dq[q % 2]).  The
+            // last tile-block's epilogue is deferred past the stage barrier;
+            // before the first stage the deferred one is an exact no-op (a
+            // zero scale pair on the bias tile, whose p is 0).
+            v16i dq[2];
+            dq[0] = bias;
+            dq[1] = bias;
+            float2 wp_pend = make_float2(0.0f, 0.0f);
+            float as_pend = 0.0f;
+            for (int st = 0; st < nstages; ++st) {
+                const bool ahead = st + 2 < nstages;
+                const int rs2 = rs == 0 ? kRing - 1 : rs - 1;
+                const StagedStage<TN>& sg = ring[rs];
+                const float4 a4 = *reinterpret_cast<const float4*>(&sg.as[as_row][0]);
+                const float as4[kSB] = {a4.x, a4.y, a4.z, a4.w};
+                // raw weight scale of block s for tile t
+                auto ws_of = [&](int s, int t) {
+                    const int wrow = (t0 + t) * kTile + col;
+                    return WS_ROWMAJOR ? sg.ws[wrow * kSB + s] : sg.ws[s * kWSRows + wrow];
+                };
+                auto a_frag = [&](int s) {
+                    return *reinterpret_cast<const v4i*>(sg.a + mw * kTile * kSeg + frag_off[s]);
+                };
+                auto w_frag = [&](int s, int t) {
+                    return *reinterpret_cast<const v4i*>(sg.w + (t0 + t) * kTile * kSeg + frag_off[s]);
+                };
+                v4i af = a_frag(0);
+                v4i wf[NT];
+                float wsv[kSB][NT];  // constant indices only: registers
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    wf[t] = w_frag(0, t);
+                    wsv[0][t] = ws_of(0, t);
+                }
+#pragma unroll
+                for (int s = 0; s < kSB; ++s) {
+                    fetch_slice(st + 2, rs2, s, ahead);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const int q = s * NT + t;
+                        if (q == 0) {
+                            // the deferred epilogue of the previous stage
+                            // covers the fragment reads of this one
+                            epilogue(dq[1], wp_pend, as_pend, acc[NT - 1]);
+                            dq[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf[0], bias, 0, 0, 0);
+                        } else {
+                            dq[q & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf[t], bias, 0, 0, 0);
+                        }
+                        if (t == NT - 1 && s + 1 < kSB) {
+                            // operands of block s + 1, read after their
+                            // registers' last MFMA has been issued
+                            af = a_frag(s + 1);
+#pragma unroll
+                            for (int tt = 0; tt < NT; ++tt) {
+                                wf[tt] = w_frag(s + 1, tt);
+                                wsv[s + 1][tt] = ws_of(s + 1, tt);
+                            }
+                        }
+                        if (q > 0) {
+                            const int sp = (q - 1) / NT, tp = (q - 1) % NT;
+                            epilogue(dq[(q - 1) & 1], ws_pair(wsv[sp][tp]), as4[sp], acc[tp]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                wp_pend = ws_pair(wsv[kSB - 1][NT - 1]);
+                as_pend = as4[kSB - 1];
+                wait_vmcnt_stage();
+                // Bare barrier (no fence): the loads of stage st + 2 stay in flight.
+                __builtin_amdgcn_s_barrier();
+                rs = rs == kRing - 1 ? 0 : rs + 1;
+            }
+            epilogue(dq[1], wp_pend, as_pend, acc[NT - 1]);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int j = j0 + (t0 + t) * kTile + col;
