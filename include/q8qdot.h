@@ -132,8 +132,10 @@ int q8_qdot_partials(const int8_t *A, const int8_t *W, int32_t *P,
                      int M, int N, int K, void *stream);
 
 /*
- * The kernel a shape dispatches to: 0 = wave64 matvec (M < 8; one A row per
- * grid row); for M >= 8 the int8-MFMA block GEMM, 1 = one workgroup per
+ * The kernel a shape dispatches to: 0 = wave64 matvec (M < 8: with K <=
+ * 16384 the 2..7 activation rows are staged together so the weights are read
+ * once; longer rows take one activation row per grid row); for M >= 8 the
+ * int8-MFMA block GEMM, 1 = one workgroup per
  * 32 x 32 output tile with the K/32 blocks split across its waves (few
  * tiles: small M or N), 2 = LDS-staged 128 x 224 workgroup tiles (large M
  * and N).  Q8_EINVAL for bad shapes.
