@@ -11,7 +11,8 @@ weights from HBM, as a decode step would.
 
 Printed: one JSON line with the headline metric (weight GB/s of the M=1
 matvec), the roofline of the dominant kernel (HBM), the batched M=512 qGEMM
-as a second measured workload (int8 TOPS, MFMA and VALU rooflines), and the
+as a second measured workload (int8 TOPS, MFMA and VALU rooflines), the
+other workloads, entry points and the GPU quantizer timed briefly, and the
 CPU oracle timed on this host on a bounded sample of the headline workload.
 """
 from __future__ import annotations
@@ -130,6 +131,45 @@ def time_launches(torch, q8, ops: Operands, steps: int, warmup: int):
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end)
     return ms / steps, wall
+
+
+def time_quantize(torch, q8, rows: int, K: int, steps: int, warmup: int, rotate: bool):
+    """q8_quantize of seeded N(0, 1) f32 rows: X f32 [rows, K] -> Q int8, D f32.
+
+    Algorithmic bytes per launch: 4 per value read, 1 per value + 4 per 32
+    values written.  R distinct copies of X (and outputs) rotate so that X
+    comes from HBM.
+    """
+    dev = torch.device("cuda:0")
+    X = torch.from_numpy(synth.random_f32((rows, K), 6000 + rows)).to(dev)
+    per = rows * K * 4 + rows * K + rows * (K // 32) * 4
+    R = max(1, -(-CACHE_DEFEAT_BYTES // per)) if rotate else 1
+    bufs = []
+    for r in range(R):
+        x = X if r == 0 else X.clone()
+        bufs.append((x, torch.empty((rows, K), dtype=torch.int8, device=dev),
+                     torch.empty((rows, K // 32), dtype=torch.float32, device=dev)))
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    ptrs = [(x.data_ptr(), q.data_ptr(), d.data_ptr()) for x, q, d in bufs]
+    for k in range(warmup):
+        st = q8.q8_quantize_raw(*ptrs[k % R], rows, K, sptr)
+        if st:
+            raise RuntimeError("q8_quantize failed: %s" % q8.q8_strerror(st))
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(steps):
+        q8.q8_quantize_raw(*ptrs[k % R], rows, K, sptr)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    gbs = per / (ms * 1e-3) / 1e9
+    del bufs
+    return {"entry": "q8_quantize", "rows": rows, "K": K, "us_per_launch": round(ms * 1e3, 3),
+            "bytes": per, "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "rotated_copies": R}
 
 
 def kernel_source_sha(path: str) -> str:
@@ -343,6 +383,19 @@ def main():
             % (rec["entry"], vw.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"],
                rec["int8_tops"]))
         del ops
+        torch.cuda.empty_cache()
+
+    # The GPU Q8_0 quantizer (the step that makes A and AS): the prompt's
+    # activation rows and a whole weight, f32 in, int8 + f32 scales out.
+    quant = [] if (args.no_variants or args.profile) else [(512, 4096), (14336, 4096)]
+    if quant:
+        result["quantize"] = []
+    for rows, K in quant:
+        rec = time_quantize(torch, q8, rows, K, max(20, args.steps // 4), max(3, args.warmup // 4),
+                            rotate=not args.no_rotate)
+        result["quantize"].append(rec)
+        log("[bench] q8_quantize %dx%d: %.3f us/launch, %.1f GB/s (%.1f%% HBM)"
+            % (rows, K, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"]))
         torch.cuda.empty_cache()
 
     if args.cpu_seconds > 0:
