@@ -169,7 +169,7 @@ Q8_API const char* q8_strerror(int status) {
         case Q8_EINVAL: return "invalid shape: M, N, K must be >= 0 and K a multiple of 32";
         case Q8_ENULL: return "null pointer for an operand the call must dereference";
         case Q8_EALIGN: return "misaligned pointer: A, W, X, Q need 16 bytes, Q5_0 weights and f32/int32 arrays 4";
-        case Q8_ERANGE: return "extent product overflows 64-bit addressing";
+        case Q8_ERANGE: return "shape out of range: an extent product overflows 64-bit addressing, or a GEMM offset 32 bits";
         case Q8_ELAUNCH: return "HIP runtime rejected the kernel launch";
         default: return "unknown status";
     }
