@@ -456,14 +456,10 @@ hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const 
     size_t smem = 0;
     if constexpr (MULTI) {
         smem = batch_smem_bytes<S>(M, PARTIALS);
-        static bool attr_set = false;  // (idempotent: a race only repeats the call)
-        if (!attr_set) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)batch_smem_bytes<S>(kMaxBatch, PARTIALS));
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        static std::atomic<uint64_t> lds_set{0};
+        const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern),
+                                             (int)batch_smem_bytes<S>(kMaxBatch, PARTIALS), lds_set);
+        if (e != hipSuccess) return e;
     }
     if (MULTI && wpc > 1 && (smem + (WST ? wst_tile_bytes(S, kT) : 0)) * wpc > 160 * 1024) wpc = 1;
     const int cap = device_cu_count() * wpc * (kT / kWave);

@@ -7,7 +7,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace q8 {
+
+// Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device, once
+// per device: the attribute is set per device, so `done` (one per kernel,
+// owned by the caller) keeps a bit per device ordinal below 64 (others are
+// set on every call).  Concurrent first calls only repeat the setting.
+inline hipError_t set_dynamic_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_relaxed) & bit) != 0) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
 
 // M < 8: wave64 matvec.  K <= 16 KiB: one kernel for one activation row or
 // (2 <= M <= 7) for all rows at once, every weight row read once; longer

@@ -461,13 +461,9 @@ hipError_t launch_staged_v(const int8_t* A, const float* AS, const int8_t* W, co
     constexpr size_t smem = need > 82 * 1024 ? need : 82 * 1024;
     static_assert(smem <= 160 * 1024, "LDS budget");
     auto kern = qgemm_staged_kernel<TN, PARTIALS, WSM>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)smem, lds_set);
+    if (e != hipSuccess) return e;
     kern<<<dim3((unsigned)total), kStagedThreads, smem, stream>>>(
         A, AS, W, WS, C, P, M, N, K, tiles_m, (int)total);
     return hipGetLastError();

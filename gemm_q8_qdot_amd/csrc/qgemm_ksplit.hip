@@ -302,13 +302,9 @@ hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const fl
     static_assert(smem <= 160 * 1024, "LDS budget");
     auto kern = qgemm_ksplit_kernel<NW, PF, PARTIALS, WST, Q5>;
     if (smem > 64 * 1024) {
-        static bool attr_set = false;
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        static std::atomic<uint64_t> lds_set{0};
+        const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)smem, lds_set);
+        if (e != hipSuccess) return e;
     }
     kern<<<dim3((unsigned)total), NW * kWave, smem, stream>>>(A, AS, W, WS, C, P, M, N, K,
                                                              (int)m_tiles, (int)total);
