@@ -57,6 +57,24 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     float* as_lds = reinterpret_cast<float*>(a_lds + K);
     const __amdgpu_buffer_rsrc_t rW5 = buffer_rsrc(W5, (int64_t)N * row_bytes);
 
+    const int groups = (N + R - 1) / R;
+    // A group's bytes: contiguous 16-byte pieces (the resource zeroes pieces
+    // past the array; pieces past the group are not needed).  The next
+    // group's pieces are loaded into registers while this group, already
+    // parked in LDS, is decoded and computed.
+    v4i piece[kPieceRounds];
+    auto load_group = [&](int g) {
+        const int gbase = g * R * row_bytes;
+#pragma unroll
+        for (int s = 0; s < kPieceRounds; ++s) {
+            const int pc = lane + kWave * s;
+            piece[s] = buffer_load16(rW5, pc < pieces ? gbase + 16 * pc : kNoRead, 0);
+        }
+    };
+    // The first group's pieces are in flight while the activation row is
+    // staged (its latency and theirs overlap).
+    if (wave < groups) load_group(wave);
+
     // The activation row and its scales, read once per workgroup (not once
     // per wave) and shared through LDS.
     for (int idx = threadIdx.x * 16; idx < K; idx += kQ5Threads * 16)
@@ -81,21 +99,6 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         a_sum[t] = dot16(a_hi[t], v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101}, s);
     }
 
-    const int groups = (N + R - 1) / R;
-    // A group's bytes: contiguous 16-byte pieces (the resource zeroes pieces
-    // past the array; pieces past the group are not needed).  The next
-    // group's pieces are loaded into registers while this group, already
-    // parked in LDS, is decoded and computed.
-    v4i piece[kPieceRounds];
-    auto load_group = [&](int g) {
-        const int gbase = g * R * row_bytes;
-#pragma unroll
-        for (int s = 0; s < kPieceRounds; ++s) {
-            const int pc = lane + kWave * s;
-            piece[s] = buffer_load16(rW5, pc < pieces ? gbase + 16 * pc : kNoRead, 0);
-        }
-    };
-    if (wave < groups) load_group(wave);
     for (int g = wave; g < groups; g += nwaves) {
         const int j0 = g * R;
         float ws[R][T];
