@@ -341,70 +341,109 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 
     if constexpr (WST) {
         // Workgroup wgx owns the rows [r_lo, r_hi) (a contiguous share) and
-        // takes them in tiles of up to kTile rows: the tile's scales of every
-        // block are staged through LDS ([row][block], padded against bank
-        // conflicts) by the whole workgroup from runs of WST that are
-        // contiguous in the row index, then its waves take the tile's rows
-        // in turn with no further barrier.  Every wave of the workgroup runs
-        // the same tiles (the staging uses barriers).
+        // takes them in tiles of up to kTile rows.  The tile's scales of
+        // every block are staged through LDS ([row][block], padded against
+        // bank conflicts) by the whole workgroup from runs of WST that are
+        // contiguous in the row index; each wave then takes the tile's rows
+        // wv, wv + kRowsWG, ... with two rows in flight (one for rows over
+        // 12 KiB).  The staging comes in two parts so that the first rows do
+        // not wait for the whole tile: the scales of the first two rows of
+        // every wave (the head) are requested first, then those rows, then
+        // the scales of the rest of the tile, which are written to LDS after
+        // each wave has finished its first two rows.  (Loads return in
+        // order: a head row's data is usable once the head scales are in,
+        // not the whole tile's.)  Every wave runs the same tiles and reaches
+        // every barrier.  Rows past the tile's end are loaded through a
+        // zero-length descriptor (no memory access), so that every wave
+        // issues the same loads and each wait covers exactly the loads it
+        // needs.
         constexpr int kRowsWG = T / kWave;
         constexpr int kKBMax = S * (kStepBytes / kBlock);
         constexpr int kPitch = kKBMax + 1;
         constexpr int kTile = wst_tile_rows(S, T);
-        constexpr int kStagePer = (kTile * kKBMax + T - 1) / T;
+        constexpr bool kTwo = S <= 12;  // two rows of 16 KiB would spill
+        constexpr int kHead = kTwo ? (2 * kRowsWG < kTile ? 2 * kRowsWG : kTile) : kTile;
+        constexpr int kRest = kTile - kHead;
+        constexpr int kHeadPer = (kHead * kKBMax + T - 1) / T;
+        constexpr int kRestPer = kRest > 0 ? (kRest * kKBMax + T - 1) / T : 1;
+        static_assert(kTile % kRowsWG == 0, "a tile holds whole rounds of rows");
         __shared__ float ws_tile[kTile * kPitch];
         const __amdgpu_buffer_rsrc_t rWST = buffer_rsrc(WS, (int64_t)KB * N * 4);
-        const int wv = (int)(threadIdx.x / kWave);
+        const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
         const int r_lo = (int)((int64_t)N * wgx / nwg);
         const int r_hi = (int)((int64_t)N * (wgx + 1) / nwg);
         float ws[S];
+        // row j's weights, or zeros without a memory access when !valid
+        auto load_row_or_zero = [&](int j, bool valid, v4i (&w)[S]) {
+            const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(W + (int64_t)(valid ? j : 0) * K, valid ? K : 0);
+#pragma unroll
+            for (int s = 0; s < S; ++s) w[s] = buffer_load16_nt(rW, lo + s * kStepBytes, 0);
+        };
         stage_batch();
         for (int t0 = r_lo; t0 < r_hi; t0 += kTile) {
             const int t1 = t0 + kTile < r_hi ? t0 + kTile : r_hi;
-            int j = t0 + wv;
-            // this wave's first rows of the tile are in flight during the staging
-            v4i w0[S], w1[S];
-            if (j < t1) load_row(j, w0, ws);
-            if constexpr (S <= 12)
-                if (j + kRowsWG < t1) load_row(j + kRowsWG, w1, ws);
-            float st[kStagePer];
+            const int j0 = t0 + wv;
+            // consecutive threads: consecutive rows of one block
+            float sh[kHeadPer], sr[kRestPer];
 #pragma unroll
-            for (int u = 0; u < kStagePer; ++u) {
-                // consecutive threads: consecutive rows of one block
+            for (int u = 0; u < kHeadPer; ++u) {
                 const int idx = threadIdx.x + u * T;
-                const int b = idx / kTile, r = idx % kTile;
-                st[u] = buffer_load_f32(rWST, (b < KB && t0 + r < t1) ? (b * N + t0 + r) * 4 : kNoRead, 0);
+                const int b = idx / kHead, r = idx % kHead;
+                sh[u] = buffer_load_f32(rWST, (b < KB && t0 + r < t1) ? (b * N + t0 + r) * 4 : kNoRead, 0);
+            }
+            v4i w0[S], w1[S];
+            load_row_or_zero(j0, j0 < t1, w0);
+            if constexpr (kTwo) load_row_or_zero(j0 + kRowsWG, j0 + kRowsWG < t1, w1);
+            if constexpr (kRest > 0) {
+#pragma unroll
+                for (int u = 0; u < kRestPer; ++u) {
+                    const int idx = threadIdx.x + u * T;
+                    const int b = idx / kRest, r = kHead + idx % kRest;
+                    sr[u] = buffer_load_f32(rWST, (b < KB && t0 + r < t1) ? (b * N + t0 + r) * 4 : kNoRead, 0);
+                }
             }
             // the previous tile's reads of ws_tile are done (no wait on loads)
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-            for (int u = 0; u < kStagePer; ++u) {
+            for (int u = 0; u < kHeadPer; ++u) {
                 const int idx = threadIdx.x + u * T;
-                const int b = idx / kTile, r = idx % kTile;
-                if (b < kKBMax) ws_tile[r * kPitch + b] = st[u];
+                const int b = idx / kHead, r = idx % kHead;
+                if (b < kKBMax) ws_tile[r * kPitch + b] = sh[u];
             }
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             auto tile_ws = [&](int jj) {
 #pragma unroll
                 for (int s = 0; s < S; ++s) ws[s] = ws_tile[(jj - t0) * kPitch + (s * kStepBytes + lo) / kBlock];
             };
-            if constexpr (S <= 12) {
-                // two rows in flight: each row's compute is followed by the
-                // load of the row two steps ahead into its registers
-                while (j < t1) {
+            if constexpr (kTwo) {
+                // the head rows; each row's compute is followed by the load
+                // of the row two rounds ahead into its registers
+                if (j0 < t1) { tile_ws(j0); compute_row(j0, w0, ws); }
+                load_row_or_zero(j0 + 2 * kRowsWG, j0 + 2 * kRowsWG < t1, w0);
+                if (j0 + kRowsWG < t1) { tile_ws(j0 + kRowsWG); compute_row(j0 + kRowsWG, w1, ws); }
+                load_row_or_zero(j0 + 3 * kRowsWG, j0 + 3 * kRowsWG < t1, w1);
+                if constexpr (kRest > 0) {
+#pragma unroll
+                    for (int u = 0; u < kRestPer; ++u) {
+                        const int idx = threadIdx.x + u * T;
+                        const int b = idx / kRest, r = kHead + idx % kRest;
+                        if (b < kKBMax) ws_tile[r * kPitch + b] = sr[u];
+                    }
+                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                }
+                for (int j = j0 + 2 * kRowsWG; j < t1; j += 2 * kRowsWG) {
                     const int j1 = j + kRowsWG;
                     tile_ws(j);
                     compute_row(j, w0, ws);
-                    if (j1 + kRowsWG < t1) load_row(j1 + kRowsWG, w0, ws);
+                    load_row_or_zero(j + 2 * kRowsWG, j + 2 * kRowsWG < t1, w0);
                     if (j1 >= t1) break;
                     tile_ws(j1);
                     compute_row(j1, w1, ws);
-                    if (j1 + 2 * kRowsWG < t1) load_row(j1 + 2 * kRowsWG, w1, ws);
-                    j = j1 + kRowsWG;
+                    load_row_or_zero(j1 + 2 * kRowsWG, j1 + 2 * kRowsWG < t1, w1);
                 }
             } else {
-                for (; j < t1; j += kRowsWG) {
-                    if (j != t0 + wv) load_row(j, w0, ws);
+                for (int j = j0; j < t1; j += kRowsWG) {
+                    if (j != j0) load_row_or_zero(j, true, w0);
                     tile_ws(j);
                     compute_row(j, w0, ws);
                 }
