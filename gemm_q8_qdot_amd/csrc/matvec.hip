@@ -201,12 +201,14 @@ matvec_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 // Several rows (MULTI, 2 <= M <= 7): the workgroup stages all of them and
 // their scales in LDS once, and every 16-byte weight piece is dotted with
 // the M activation pieces read back from LDS, so the weights cross the bus
-// once for all rows.  Launch shape, measured on MI355X: rows of up to 8 KiB
-// run one 8-wave workgroup per compute unit; longer rows run one 4-wave
-// workgroup per compute unit with the next row's loads issued before the
-// current row is computed (PF).  Fewer bytes in flight per compute unit than
-// either made the stream slower; more (more waves, or several workgroups per
-// compute unit) made it slower too.
+// once for all rows.  Launch shape for one activation row, measured on
+// MI355X: each wave has one weight row in flight; rows of up to 8 KiB run
+// one 8-wave workgroup per compute unit, rows of 9..14 KiB one 4-wave
+// workgroup (36..56 KiB in flight per compute unit), rows of 15 or 16 KiB
+// one 8-wave workgroup.  Two rows in flight per wave (the next row's loads
+// issued before the current row is computed) or eight waves on rows of
+// 9..14 KiB streamed 3-4 % slower; fewer bytes in flight than this on short
+// rows made the stream slower too.
 // WST: weight scales stored transposed, [K/32][N] (qmma_t), staged through
 // LDS per tile of rows (see below).
 constexpr int kMaxBatch = 7;
@@ -225,7 +227,7 @@ constexpr size_t batch_smem_bytes(int M, bool partials) {
     return (size_t)M * S * kStepBytes + (partials ? 0 : (size_t)M * (S * (kStepBytes / kBlock) + 64) * 4);
 }
 
-template <int S, bool PF, bool PARTIALS, bool WST, bool MULTI, int T>
+template <int S, bool PARTIALS, bool WST, bool MULTI, int T>
 __global__ void __launch_bounds__(T)
 matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                    const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -449,23 +451,6 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                 }
             }
         }
-    } else if constexpr (PF) {
-        // Two rows in flight: ping-pong registers, loop unrolled by two.
-        v4i w0[S], w1[S];
-        float ws0[S], ws1[S];
-        int j = wave;
-        if (j < N) load_row(j, w0, ws0);
-        stage_batch();
-        while (j < N) {
-            const int j1 = j + nwaves;
-            if (j1 < N) load_row(j1, w1, ws1);
-            compute_row(j, w0, ws0);
-            if (j1 >= N) break;
-            const int j2 = j1 + nwaves;
-            if (j2 < N) load_row(j2, w0, ws0);
-            compute_row(j1, w1, ws1);
-            j = j2;
-        }
     } else {
         v4i w[S];
         float ws[S];
@@ -481,17 +466,14 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 template <int S, bool PARTIALS, bool WST, bool MULTI>
 hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    // Launch shapes, measured on MI355X.  One row: rows of up to 8 KiB, one
-    // 8-wave workgroup per compute unit; rows of 9..14 KiB, one 4-wave
-    // workgroup with the next row prefetched (PF; two rows of 15 or 16 KiB
-    // in registers would spill).  A batch of rows (more work per weight
-    // byte, so more waves to hide it): 8-wave workgroups, two per compute
-    // unit when their LDS fits (one with transposed scales on rows over
-    // 4 KiB, whose tiles then split worse).
-    constexpr bool kPF = !WST && !MULTI && S > 8 && S <= 14;
-    constexpr int kT = kPF ? 256 : 512;
+    // Launch shapes, measured on MI355X.  One row: rows of 9..14 KiB run one
+    // 4-wave workgroup per compute unit, other rows one 8-wave workgroup.  A
+    // batch of rows (more work per weight byte, so more waves to hide it):
+    // 8-wave workgroups, two per compute unit when their LDS fits (one with
+    // transposed scales on rows over 4 KiB, whose tiles then split worse).
+    constexpr int kT = (!WST && !MULTI && S > 8 && S <= 14) ? 256 : 512;
     int wpc = (MULTI && !(WST && S > 4)) ? 2 : 1;  // workgroups per compute unit
-    auto kern = matvec_rows_kernel<S, kPF, PARTIALS, WST, MULTI, kT>;
+    auto kern = matvec_rows_kernel<S, PARTIALS, WST, MULTI, kT>;
     size_t smem = 0;
     if constexpr (MULTI) {
         smem = batch_smem_bytes<S>(M, PARTIALS);
