@@ -27,7 +27,6 @@ namespace {
 constexpr int kQ5Threads = 256;
 constexpr int kQ5BlockBytes = 20;
 constexpr int kQ5MaxT = 8;               // K <= 64 * 8 blocks (16 Ki values) resident
-constexpr int kQ5MaxWaves = 256 * 8;     // eight waves per CU, each walking several row groups
 
 // WST: weight scales stored transposed, [K/32][N] (q50_qmma_t).
 // A wave reads its R weight rows as contiguous 16-byte pieces (lane l takes
@@ -158,13 +157,21 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 template <int T, bool PARTIALS, bool WST>
 hipError_t launch_q5_t(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS,
                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    constexpr int R = T == 1 ? 4 : (T == 2 ? 2 : 1);  // short rows: several per wave
+    // Launch shape, measured on MI355X (N=14336): rows of 2 KiB or less go
+    // four to a wave group, eight waves per compute unit; rows of 65..192
+    // blocks (K = 2080..6144) one per group, sixteen waves per compute unit
+    // (K=4096: 11.0 -> 10.5 us against two rows per group and eight waves;
+    // K=6144: 15.4 -> 14.2 us); longer rows one per group, eight waves (at
+    // K=8192 sixteen tie, at K=14336 they are 12 % slower).
+    constexpr int R = T == 1 ? 4 : 1;
+    constexpr int kWavesPerCU = (T == 2 || T == 3) ? 16 : 8;
     constexpr int kPieceRounds = (R * T * kWave * kQ5BlockBytes + kWave * 16 - 1) / (kWave * 16);
     // per-wave weight staging areas, then the activation row and its scales
     const size_t smem = (size_t)(kQ5Threads / kWave) * kPieceRounds * kWave * 16 + (size_t)K +
                         (size_t)(K / kBlock) * 4;
     const int groups = (N + R - 1) / R;
-    const int waves = groups < kQ5MaxWaves ? groups : kQ5MaxWaves;
+    const int max_waves = device_cu_count() * kWavesPerCU;
+    const int waves = groups < max_waves ? groups : max_waves;
     const int wgs = (waves + kQ5Threads / kWave - 1) / (kQ5Threads / kWave);
     matvec_q50_kernel<T, R, PARTIALS, WST><<<dim3(wgs, M), kQ5Threads, smem, stream>>>(
         A, AS, W5, WS, C, P, N, K);
