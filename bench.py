@@ -365,6 +365,7 @@ def main():
         ("qmma", synth.WORKLOADS[1]), ("qmma", synth.WORKLOADS[4]),
         ("q50", synth.WORKLOADS[1]), ("q50", synth.WORKLOADS[2]), ("q50", synth.WORKLOADS[3]),
         ("qdot", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
+        ("q50", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
     ]
     if variants:
         result["variants"] = []

@@ -4,7 +4,9 @@ q8_q50_partials) against the oracle's q50 definitions, element by element.
 Bar: int32 partials bit-exact; f32 within ``1e-5 * sum_b |AS*WS*P| + 1e-6``.
 Weights are seeded uniform bytes (every byte pattern is a valid Q5_0
 block), so all 32 codes and all qh bit patterns occur.  Shapes reach the
-one-row matvec (M < 8, K <= 16384) and the K-split GEMM (everything else),
+matvec (M < 8, K <= 16384: one activation row, a batch staged in LDS, or a
+batch too large for LDS taken a row at a time) and the K-split GEMM
+(everything else),
 blocks per row not a multiple of 4 (rows that start 4- but not 16-byte
 aligned), ragged M and N, and a weight array that starts 4 bytes past a
 16-byte boundary.
@@ -81,6 +83,13 @@ SHAPES = [
     (1, 14336, 4096), (1, 4096, 14336), (1, 37, 96), (3, 129, 2080), (7, 300, 1024),  # matvec
     (1, 9, 16416), (2, 100, 16416),                                                     # K-split, long K
     (8, 37, 96), (64, 4096, 4096), (127, 300, 4160), (512, 1024, 4096), (33, 65, 160),  # K-split
+    # small batches read the weights once for all rows when the rows fit in
+    # LDS: four rows to a weight group (K <= 2048), one row of 65..96 blocks
+    # (blocks past K/32 in some lanes), 96..448 blocks, the largest rows at
+    # M = 2 and 3; larger batches of long rows fall back to one grid row per
+    # activation row
+    (7, 4096, 2048), (2, 1, 32), (4, 14336, 4096), (5, 333, 2080), (2, 3000, 6144),
+    (5, 1000, 8192), (3, 500, 14336), (2, 65, 16384), (6, 777, 14336), (7, 129, 16384),
 ]
 
 
