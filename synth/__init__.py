@@ -119,3 +119,31 @@ def random_q50(rows: int, K: int, seed: int) -> np.ndarray:
     """
     rng = np.random.default_rng(seed)
     return rng.integers(0, 256, size=(rows, K // 32 * 20), dtype=np.uint8)
+
+
+def cancelling_blocks(M: int, N: int, K: int, seed: int):
+    """Operands whose half-block sums are large and cancel within each block.
+
+    Every activation block repeats its first 16 bytes in its second half;
+    every weight block's second half is the negated first half with one byte
+    moved by one.  The two half-block dot products are then +-(65..260)
+    thousand while the block sum P (exact in int32) is a single a*(+-1)
+    term, so |P| <= 127.  The contraction's tolerance scales with
+    sum_b |AS*WS*P|, so arithmetic that scaled and rounded half-block sums
+    before forming P misses it on most outputs.  Only byte patterns and
+    seeded scales are made here; nothing of the contraction is computed.
+    """
+    rng = np.random.default_rng(seed)
+    KB = K // 32
+    # magnitudes 64..127 with one sign per (block, position) shared by A and
+    # W, so every half-block product is positive and the halves are large
+    sign = np.where(rng.random((1, KB, 16)) < 0.5, -1, 1).astype(np.int16)
+    a = sign * rng.integers(64, 128, size=(M, KB, 16), dtype=np.int16)
+    w = sign * rng.integers(64, 128, size=(N, KB, 16), dtype=np.int16)
+    A = np.concatenate([a, a], axis=2).reshape(M, K).astype(np.int8)
+    w_hi = -w
+    w_hi[:, :, 0] = np.where(w_hi[:, :, 0] < 127, w_hi[:, :, 0] + 1, w_hi[:, :, 0] - 1)
+    W = np.concatenate([w, w_hi], axis=2).reshape(N, K).astype(np.int8)
+    AS = random_scales((M, KB), seed + 1, 1e-3, 1.0)
+    WS = random_scales((N, KB), seed + 2, 1e-3, 1.0)
+    return A, AS, W, WS

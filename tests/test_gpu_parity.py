@@ -171,6 +171,21 @@ def test_small_batch(dev, M, N, K):
     _check_full(A, AS, W, WS, dev, "batch")
 
 
+# one row, a small batch, the K-split GEMM, the LDS-staged GEMM
+@pytest.mark.parametrize("M,N,K", [(1, 3000, 4096), (4, 3000, 4096), (64, 512, 2048), (256, 14336, 256)])
+def test_cancelling_half_blocks(dev, M, N, K):
+    A, AS, W, WS = synth.cancelling_blocks(M, N, K, 880 + M)
+    P = oracle.block_partials(A, W)
+    assert np.abs(P).max() <= 128                      # the construction holds
+    C, _ = _check_full(A, AS, W, WS, dev, "cancelling halves")
+    # the transposed-scale entry takes the same care
+    WST = np.ascontiguousarray(WS.T)
+    C2 = q8.q8_qmma(_dev(A, dev), _dev(AS, dev), _dev(W, dev), _dev(WST, dev))
+    torch.cuda.synchronize()
+    out, mag = oracle.qmma_f64(A, AS, W, WST)
+    _assert_close(C2.cpu().numpy(), out, mag, "cancelling halves (qmma)")
+
+
 @pytest.mark.parametrize("M,N,K", EDGE)
 def test_edge_shapes(dev, M, N, K):
     seed = M * 1000003 + N * 101 + K

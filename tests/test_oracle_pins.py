@@ -378,3 +378,33 @@ def test_q50_partials_equal_q8_partials_of_decoded_values():
     P8 = oracle.block_partials(A, oracle.q50_decode(W5, 320))
     assert np.array_equal(P5, P8)
     assert np.abs(P5).max() <= 32 * 128 * 16
+
+
+def test_cancelling_blocks_discriminate_half_block_scaling():
+    # The GPU parity test built on synth.cancelling_blocks is only worth
+    # something if the tolerance rejects arithmetic that scales half-block
+    # sums before the exact block sum is formed.  Check that here, on the
+    # host: the construction holds, an f32 accumulation of the exact block
+    # sums passes the bar everywhere, and the same accumulation fed the two
+    # half-block sums separately fails it on most outputs.
+    M, N, K = 3, 200, 2048
+    A, AS, W, WS = synth.cancelling_blocks(M, N, K, 17)
+    KB = K // 32
+    Ab = A.reshape(M, KB, 32).astype(np.int64)
+    Wb = W.reshape(N, KB, 32).astype(np.int64)
+    lo = np.einsum("mbt,nbt->mnb", Ab[:, :, :16], Wb[:, :, :16])
+    hi = np.einsum("mbt,nbt->mnb", Ab[:, :, 16:], Wb[:, :, 16:])
+    P = oracle.block_partials(A, W)
+    assert np.array_equal(P, lo + hi)
+    assert np.abs(P).max() <= 127 and np.abs(lo).min() >= 60000
+    out, mag = oracle.qdot_f64(A, AS, W, WS)
+    s = AS[:, None, :] * WS[None, :, :]                 # f32 products
+    exact = np.zeros((M, N), np.float32)
+    halves = np.zeros((M, N), np.float32)
+    for b in range(KB):
+        exact = exact + s[:, :, b] * P[:, :, b].astype(np.float32)
+        halves = halves + s[:, :, b] * lo[:, :, b].astype(np.float32)
+        halves = halves + s[:, :, b] * hi[:, :, b].astype(np.float32)
+    assert exact.dtype == np.float32 and halves.dtype == np.float32
+    assert oracle.within_tolerance(exact, out, mag).all()
+    assert oracle.within_tolerance(halves, out, mag).mean() < 0.7
