@@ -463,15 +463,9 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     }
 }
 
-template <int S, bool PARTIALS, bool WST, bool MULTI>
-hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                       float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    // Launch shapes, measured on MI355X.  One row: rows of 9..14 KiB run one
-    // 4-wave workgroup per compute unit, other rows one 8-wave workgroup.  A
-    // batch of rows (more work per weight byte, so more waves to hide it):
-    // 8-wave workgroups, two per compute unit when their LDS fits (one with
-    // transposed scales on rows over 4 KiB, whose tiles then split worse).
-    constexpr int kT = (!WST && !MULTI && S > 8 && S <= 14) ? 256 : 512;
+template <int S, bool PARTIALS, bool WST, bool MULTI, int kT>
+hipError_t launch_rows_t(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                         float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     int wpc = (MULTI && !(WST && S > 4)) ? 2 : 1;  // workgroups per compute unit
     auto kern = matvec_rows_kernel<S, PARTIALS, WST, MULTI, kT>;
     size_t smem = 0;
@@ -488,6 +482,30 @@ hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const 
     const int wgs = (waves + kT / kWave - 1) / (kT / kWave);
     kern<<<dim3(wgs, MULTI ? 1 : M), kT, smem, stream>>>(A, AS, W, WS, C, P, M, N, K);
     return hipGetLastError();
+}
+
+template <int S, bool PARTIALS, bool WST, bool MULTI>
+hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                       float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
+    // Launch shapes, measured on MI355X.  One row: rows of 9..14 KiB run one
+    // 4-wave workgroup per compute unit; rows of 4..8 KiB one 7-wave
+    // workgroup when seven waves per compute unit leave no more row slots
+    // per compute unit than eight (N=14336, K=4096: 11.55 -> 11.3 us; at
+    // N=4096 seven waves would leave some waves a third row), else one
+    // 8-wave workgroup, as for shorter and longer rows.  A batch of rows
+    // (more work per weight byte, so more waves to hide it): 8-wave
+    // workgroups, two per compute unit when their LDS fits (one with
+    // transposed scales on rows over 4 KiB, whose tiles then split worse).
+    if constexpr (!WST && !MULTI && S > 8 && S <= 14)
+        return launch_rows_t<S, PARTIALS, WST, MULTI, 256>(A, AS, W, WS, C, P, M, N, K, stream);
+    if constexpr (!WST && !MULTI && S >= 4 && S <= 8) {
+        const int64_t cus = device_cu_count();
+        const int64_t slots7 = ((int64_t)N + 7 * cus - 1) / (7 * cus) * 7;
+        const int64_t slots8 = ((int64_t)N + 8 * cus - 1) / (8 * cus) * 8;
+        if (slots7 <= slots8)
+            return launch_rows_t<S, PARTIALS, WST, MULTI, 448>(A, AS, W, WS, C, P, M, N, K, stream);
+    }
+    return launch_rows_t<S, PARTIALS, WST, MULTI, 512>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 template <bool PARTIALS, bool WST, bool MULTI>
