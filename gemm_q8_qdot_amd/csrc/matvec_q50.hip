@@ -238,13 +238,12 @@ hipError_t launch_q5_t(const int8_t* A, const float* AS, const uint8_t* W5, cons
     // Launch shape, measured on MI355X (N=14336): rows of 2 KiB or less go
     // four to a wave group, eight waves per compute unit; rows of 65..192
     // blocks (K = 2080..6144) one per group, sixteen waves per compute unit
-    // (K=4096: 11.0 -> 10.5 us against two rows per group and eight waves;
+    // (K=4096: 11.0 -> 10.6 us against two rows per group and eight waves;
     // K=6144: 15.4 -> 14.2 us); longer rows one per group, eight waves (at
     // K=8192 sixteen tie, at K=14336 they are 12 % slower).
     constexpr int R = T == 1 ? 4 : 1;
     constexpr int kWavesPerCU = (T == 2 || T == 3) ? 16 : 8;
     constexpr int kPieceRounds = (R * T * kWave * kQ5BlockBytes + kWave * 16 - 1) / (kWave * 16);
-    // per-wave weight staging areas, then the activation row and its scales
     const int groups = (N + R - 1) / R;
     if constexpr (!PARTIALS) {
         // A batch of rows in one pass when the staged rows fit in LDS beside
@@ -267,6 +266,8 @@ hipError_t launch_q5_t(const int8_t* A, const float* AS, const uint8_t* W5, cons
             return hipGetLastError();
         }
     }
+    // one activation row per grid row: per-wave weight staging areas, then
+    // the row and its scales
     const size_t smem = (size_t)(kQ5Threads / kWave) * kPieceRounds * kWave * 16 + (size_t)K +
                         (size_t)(K / kBlock) * 4;
     const int max_waves = device_cu_count() * kWavesPerCU;
