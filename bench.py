@@ -14,6 +14,7 @@ matvec), the roofline of the dominant kernel (HBM), the batched M=512 qGEMM
 as a second measured workload (int8 TOPS, MFMA and VALU rooflines), the
 other workloads, entry points and the GPU quantizer timed briefly, and the
 CPU oracle timed on this host on a bounded sample of the headline workload.
+The GEMMs are timed last.
 """
 from __future__ import annotations
 
@@ -314,6 +315,73 @@ def main():
     del head
     torch.cuda.empty_cache()
 
+    # The small workloads, before the GEMMs.
+    others = [int(x) for x in args.others.split(",") if x.strip() != ""]
+    if others:
+        result["others"] = []
+    for idx in others:
+        ow = synth.WORKLOADS[idx]
+        ops = Operands(torch, q8, ow, rotate=not args.no_rotate)
+        ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
+        rec = {"workload": ow.name, "M": ow.M, "N": ow.N, "K": ow.K,
+               "kernel": KERNEL_NAMES[q8.q8_qdot_path(ow.M, ow.N, ow.K)],
+               "us_per_launch": round(ms3 * 1e3, 3),
+               "hbm_gbs": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9, 1),
+               "hbm_frac": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "int8_tops": round(ops.int8_ops / (ms3 * 1e-3) / 1e12, 2)}
+        result["others"].append(rec)
+        log("[bench] %s: %.3f us/launch, %.1f GB/s (%.1f%% HBM), %.1f int8 TOPS"
+            % (ow.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"], rec["int8_tops"]))
+        del ops
+        torch.cuda.empty_cache()
+
+    # The other entry points and dispatch paths, on the same workload shapes:
+    # qmma_t (transposed scales), Q5_0 weights, and a small decode batch.
+    # The qmma_t GEMM is timed with the other GEMM, last.
+    variants = [] if (args.no_variants or args.profile) else [
+        ("qmma", synth.WORKLOADS[1]),
+        ("q50", synth.WORKLOADS[1]), ("q50", synth.WORKLOADS[2]), ("q50", synth.WORKLOADS[3]),
+        ("qdot", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
+        ("q50", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
+    ]
+    late_variants = [] if (args.no_variants or args.profile) else [("qmma", synth.WORKLOADS[4])]
+    if variants or late_variants:
+        result["variants"] = []
+
+    def time_variants(todo):
+        for kind, vw in todo:
+            ops = Operands(torch, q8, vw, rotate=not args.no_rotate, kind=kind)
+            ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
+            rec = {"entry": {"qdot": "q8_qdot", "qmma": "q8_qmma", "q50": "q8_q50_qdot"}[kind],
+                   "workload": vw.name, "M": vw.M, "N": vw.N, "K": vw.K,
+                   "us_per_launch": round(ms3 * 1e3, 3),
+                   "weight_bytes": ops.weight_bytes,
+                   "hbm_gbs": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "int8_tops": round(ops.int8_ops / (ms3 * 1e-3) / 1e12, 2)}
+            result["variants"].append(rec)
+            log("[bench] %s %s: %.3f us/launch, %.1f GB/s (%.1f%% HBM), %.1f int8 TOPS"
+                % (rec["entry"], vw.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"],
+                   rec["int8_tops"]))
+            del ops
+            torch.cuda.empty_cache()
+
+    time_variants(variants)
+
+    # The GPU Q8_0 quantizer (the step that makes A and AS): the prompt's
+    # activation rows and a whole weight, f32 in, int8 + f32 scales out.
+    quant = [] if (args.no_variants or args.profile) else [(512, 4096), (14336, 4096)]
+    if quant:
+        result["quantize"] = []
+    for rows, K in quant:
+        rec = time_quantize(torch, q8, rows, K, max(20, args.steps // 4), max(3, args.warmup // 4),
+                            rotate=not args.no_rotate)
+        result["quantize"].append(rec)
+        log("[bench] q8_quantize %dx%d: %.3f us/launch, %.1f GB/s (%.1f%% HBM)"
+            % (rows, K, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"]))
+        torch.cuda.empty_cache()
+
+    # The GEMMs last.
     if args.second >= 0:
         sw = synth.WORKLOADS[args.second]
         log("[bench] preparing %s" % sw.name)
@@ -340,64 +408,7 @@ def main():
         del sec
         torch.cuda.empty_cache()
 
-    others = [int(x) for x in args.others.split(",") if x.strip() != ""]
-    if others:
-        result["others"] = []
-    for idx in others:
-        ow = synth.WORKLOADS[idx]
-        ops = Operands(torch, q8, ow, rotate=not args.no_rotate)
-        ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
-        rec = {"workload": ow.name, "M": ow.M, "N": ow.N, "K": ow.K,
-               "kernel": KERNEL_NAMES[q8.q8_qdot_path(ow.M, ow.N, ow.K)],
-               "us_per_launch": round(ms3 * 1e3, 3),
-               "hbm_gbs": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9, 1),
-               "hbm_frac": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-               "int8_tops": round(ops.int8_ops / (ms3 * 1e-3) / 1e12, 2)}
-        result["others"].append(rec)
-        log("[bench] %s: %.3f us/launch, %.1f GB/s (%.1f%% HBM), %.1f int8 TOPS"
-            % (ow.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"], rec["int8_tops"]))
-        del ops
-        torch.cuda.empty_cache()
-
-    # The other entry points and dispatch paths, on the same workload shapes:
-    # qmma_t (transposed scales), Q5_0 weights, and a small decode batch.
-    variants = [] if (args.no_variants or args.profile) else [
-        ("qmma", synth.WORKLOADS[1]), ("qmma", synth.WORKLOADS[4]),
-        ("q50", synth.WORKLOADS[1]), ("q50", synth.WORKLOADS[2]), ("q50", synth.WORKLOADS[3]),
-        ("qdot", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
-        ("q50", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
-    ]
-    if variants:
-        result["variants"] = []
-    for kind, vw in variants:
-        ops = Operands(torch, q8, vw, rotate=not args.no_rotate, kind=kind)
-        ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
-        rec = {"entry": {"qdot": "q8_qdot", "qmma": "q8_qmma", "q50": "q8_q50_qdot"}[kind],
-               "workload": vw.name, "M": vw.M, "N": vw.N, "K": vw.K,
-               "us_per_launch": round(ms3 * 1e3, 3),
-               "weight_bytes": ops.weight_bytes,
-               "hbm_gbs": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9, 1),
-               "hbm_frac": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-               "int8_tops": round(ops.int8_ops / (ms3 * 1e-3) / 1e12, 2)}
-        result["variants"].append(rec)
-        log("[bench] %s %s: %.3f us/launch, %.1f GB/s (%.1f%% HBM), %.1f int8 TOPS"
-            % (rec["entry"], vw.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"],
-               rec["int8_tops"]))
-        del ops
-        torch.cuda.empty_cache()
-
-    # The GPU Q8_0 quantizer (the step that makes A and AS): the prompt's
-    # activation rows and a whole weight, f32 in, int8 + f32 scales out.
-    quant = [] if (args.no_variants or args.profile) else [(512, 4096), (14336, 4096)]
-    if quant:
-        result["quantize"] = []
-    for rows, K in quant:
-        rec = time_quantize(torch, q8, rows, K, max(20, args.steps // 4), max(3, args.warmup // 4),
-                            rotate=not args.no_rotate)
-        result["quantize"].append(rec)
-        log("[bench] q8_quantize %dx%d: %.3f us/launch, %.1f GB/s (%.1f%% HBM)"
-            % (rows, K, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"]))
-        torch.cuda.empty_cache()
+    time_variants(late_variants)
 
     if args.cpu_seconds > 0:
         log("[bench] CPU oracle baseline (~%.0f s)" % args.cpu_seconds)
