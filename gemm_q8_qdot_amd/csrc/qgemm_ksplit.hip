@@ -22,10 +22,12 @@
 //     exchange inside one wave, ordered by the LDS queue of that wave;
 //   - per block one v_mfma_i32_32x32x32_i8 (one Q8_0 block) seeded with the
 //     f32 bias pattern, then the 2-op f32 epilogue of ws_pair.
-// Sixteen waves per workgroup (four per SIMD) hide the load latency; the
-// register double-buffered variant (Q8_KS_PREFETCH=1) needs more VGPRs than
-// four waves per SIMD allow and measured slower on MI355X.  At the end the NW partial tiles are summed in LDS in wave order (a fixed
-// order: the result is deterministic) and stored.  Tiles sharing a W slab
+// Sixteen waves per workgroup (four per SIMD) hide the load latency; a
+// register double-buffered form (each wave's next chunk loaded while the
+// current one is computed) needs more VGPRs than four waves per SIMD allow,
+// spilled, and measured 2.4x slower on MI355X.  At the end the NW partial
+// tiles are summed in LDS in wave order (a fixed order: the result is
+// deterministic) and stored.  Tiles sharing a W slab
 // (the M tiles of one N tile) get consecutive launch slots of one XCD so the
 // slab is read from HBM once.
 #include "q8_device.h"
@@ -36,9 +38,6 @@ namespace {
 
 #ifndef Q8_KS_WAVES
 #define Q8_KS_WAVES 16
-#endif
-#ifndef Q8_KS_PREFETCH
-#define Q8_KS_PREFETCH 0
 #endif
 
 constexpr int kKsWaves = Q8_KS_WAVES;  // waves per workgroup (K split)
@@ -77,7 +76,7 @@ struct KsRaw {
 // WST: weight scales stored transposed, [K/32][N] (the qmma_t form).
 // Q5: W holds Q5_0 blocks (20 bytes per 32 values; the q50 rows of the
 // Q8_0 table), decoded to signed bytes on their way into LDS.
-template <int NW, bool PF, bool PARTIALS, bool WST, bool Q5>
+template <int NW, bool PARTIALS, bool WST, bool Q5>
 __global__ void __launch_bounds__(NW * kWave)
 qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -253,22 +252,10 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const int per_wave = (nchunks + NW - 1) / NW;
     const int c_begin = wv * per_wave;
     const int c_end = min(c_begin + per_wave, nchunks);
-    if constexpr (PF) {
-        KsRaw r0, r1;
-        if (c_begin < c_end) load_chunk(r0, c_begin);
-        for (int c = c_begin; c < c_end; c += 2) {
-            if (c + 1 < c_end) load_chunk(r1, c + 1);
-            stage_and_compute(r0, c);
-            if (c + 1 >= c_end) break;
-            if (c + 2 < c_end) load_chunk(r0, c + 2);
-            stage_and_compute(r1, c + 1);
-        }
-    } else {
-        for (int c = c_begin; c < c_end; ++c) {
-            KsRaw r0;
-            load_chunk(r0, c);
-            stage_and_compute(r0, c);
-        }
+    for (int c = c_begin; c < c_end; ++c) {
+        KsRaw r0;
+        load_chunk(r0, c);
+        stage_and_compute(r0, c);
     }
 
     if constexpr (!PARTIALS) {
@@ -291,7 +278,7 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     }
 }
 
-template <int NW, bool PF, bool PARTIALS, bool WST, bool Q5>
+template <int NW, bool PARTIALS, bool WST, bool Q5>
 hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                      float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     const int64_t m_tiles = (M + kTile - 1) / kTile;
@@ -300,7 +287,7 @@ hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const fl
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     constexpr size_t smem = ksplit_smem_bytes<NW>();
     static_assert(smem <= 160 * 1024, "LDS budget");
-    auto kern = qgemm_ksplit_kernel<NW, PF, PARTIALS, WST, Q5>;
+    auto kern = qgemm_ksplit_kernel<NW, PARTIALS, WST, Q5>;
     if (smem > 64 * 1024) {
         static std::atomic<uint64_t> lds_set{0};
         const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)smem, lds_set);
@@ -316,20 +303,18 @@ hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const fl
 hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                                float* C, int32_t* P, int M, int N, int K, bool ws_t,
                                hipStream_t stream) {
-    constexpr bool pf = Q8_KS_PREFETCH != 0;
-    if (P != nullptr) return launch_ks<kKsWaves, pf, true, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
-    if (ws_t) return launch_ks<kKsWaves, pf, false, true, false>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_ks<kKsWaves, pf, false, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (P != nullptr) return launch_ks<kKsWaves, true, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_ks<kKsWaves, false, true, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks<kKsWaves, false, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 hipError_t launch_qgemm_ksplit_q50(const int8_t* A, const float* AS, const uint8_t* W5,
                                    const float* WS, float* C, int32_t* P, int M, int N, int K,
                                    bool ws_t, hipStream_t stream) {
-    constexpr bool pf = Q8_KS_PREFETCH != 0;
     const int8_t* W = reinterpret_cast<const int8_t*>(W5);
-    if (P != nullptr) return launch_ks<kKsWaves, pf, true, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
-    if (ws_t) return launch_ks<kKsWaves, pf, false, true, true>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_ks<kKsWaves, pf, false, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (P != nullptr) return launch_ks<kKsWaves, true, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_ks<kKsWaves, false, true, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks<kKsWaves, false, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
 }
 
 }  // namespace q8
