@@ -109,9 +109,13 @@ int q8_qmma(const int8_t *A, const float *AS, const int8_t *W, const float *WST,
  * library reads it as bit e of the little-endian word.)  W5 must be 4-byte
  * aligned; A 16-byte; AS, WS/WST, C, P 4-byte.  Scales as for q8_qdot_stream
  * (q8_q50_qdot: WS [N][K/32]) and q8_qmma (q8_q50_qmma: WST [K/32][N]).
- * M < 8 with K <= 16384 runs a one-row matvec per activation row; anything
- * else the K-split MFMA GEMM (for which 32 * K, and with WST (K/32) * N * 4,
- * must be below 2^31, else Q8_ERANGE).  q8_q50_partials: P[i][j][b] =
+ * M < 8 with K <= 16384 runs the Q5_0 matvec: a batch of 2..7 activation
+ * rows that fits in LDS beside the weight staging areas (up to 7 rows of
+ * K <= 8192, 6 of 12288, 5 of 14336, 4 of 16384) is taken in one pass that
+ * reads the weights once, larger ones one activation row per pass
+ * (q8_q50_partials: always one row per pass).  Anything else runs the
+ * K-split MFMA GEMM (for which 32 * K, and with WST (K/32) * N * 4, must be
+ * below 2^31, else Q8_ERANGE).  q8_q50_partials: P[i][j][b] =
  * sum over the block of A * (q - 16), int32 [M][N][K/32].
  */
 int q8_q50_qdot(const int8_t *A, const float *AS, const uint8_t *W5, const float *WS,
