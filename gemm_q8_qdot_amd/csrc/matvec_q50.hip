@@ -83,7 +83,7 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 #pragma unroll
         for (int s = 0; s < kPieceRounds; ++s) {
             const int pc = lane + kWave * s;
-            piece[s] = buffer_load16(rW5, pc < pieces ? gbase + 16 * pc : kNoRead, 0);
+            piece[s] = buffer_load16_nt(rW5, pc < pieces ? gbase + 16 * pc : kNoRead, 0);  // read once: streaming
         }
     };
     // The first group's pieces are in flight while the activation row is
