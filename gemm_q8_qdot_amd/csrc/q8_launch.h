@@ -25,6 +25,24 @@ inline hipError_t set_dynamic_lds(const void* kernel, int bytes, std::atomic<uin
     return e;
 }
 
+// Workgroups of `kernel` (`threads` each, `smem` bytes of dynamic LDS) that
+// one compute unit holds at once, as the runtime computes it from the
+// kernel's registers and LDS, at least 1.  `cache` (one per kernel and key,
+// owned by the caller, zero-initialised) holds the answer per device
+// ordinal below 64; concurrent first calls only repeat the query.
+inline int wgs_per_cu(const void* kernel, int threads, size_t smem, std::atomic<int> (&cache)[64]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+    if (dev >= 0) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, smem) != hipSuccess || n < 1) n = 1;
+    if (dev >= 0) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // M < 8: wave64 matvec.  K <= 16 KiB: one kernel for one activation row or
 // (2 <= M <= 7) for all rows at once, every weight row read once; longer
 // rows: one activation row per grid row, taken in 16 KiB chunks.
