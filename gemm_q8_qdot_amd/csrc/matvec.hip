@@ -466,9 +466,9 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 template <int S, bool PARTIALS, bool WST, bool MULTI, int kT>
 hipError_t launch_rows_t(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                          float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
-    // workgroups per compute unit (one row: three for rows of 1 KiB, two for
-    // rows of 2..3 KiB, else one; a batch: see below)
-    int wpc = MULTI ? (!(WST && S > 4) ? 2 : 1) : ((!WST && S == 1) ? 3 : ((!WST && S <= 3) ? 2 : 1));
+    // workgroups per compute unit (one row, either scale layout: three for
+    // rows of 1 KiB, two for rows of 2..3 KiB, else one; a batch: see below)
+    int wpc = MULTI ? (!(WST && S > 4) ? 2 : 1) : (S == 1 ? 3 : (S <= 3 ? 2 : 1));
     auto kern = matvec_rows_kernel<S, PARTIALS, WST, MULTI, kT>;
     size_t smem = 0;
     if constexpr (MULTI) {
@@ -498,8 +498,9 @@ hipError_t launch_rows(const int8_t* A, const float* AS, const int8_t* W, const 
                        float* C, int32_t* P, int M, int N, int K, hipStream_t stream) {
     // Launch shapes, measured on MI355X.  One row: rows of 1 KiB run three
     // 8-wave workgroups per compute unit and rows of 2..3 KiB two (N=14336:
-    // K=1024 6.8 -> 4.7-5.2 us, K=2048 8.1 -> 6.9 us against one; rows this
-    // short keep too few bytes in flight with eight waves); rows of 9..14
+    // K=1024 6.8 -> 4.7-5.2 us, K=2048 8.1 -> 6.9 us against one; with
+    // transposed scales N=40000, K=1024 14.5 -> 9.8 us; rows this short keep
+    // too few bytes in flight with eight waves); rows of 9..14
     // KiB run one 4-wave workgroup per compute unit; rows of 4..8 KiB one 7-wave
     // workgroup when seven waves per compute unit leave no more row slots
     // per compute unit than eight (N=14336, K=4096: 11.55 -> 11.3 us; at
