@@ -76,7 +76,9 @@ struct KsRaw {
 // WST: weight scales stored transposed, [K/32][N] (the qmma_t form).
 // Q5: W holds Q5_0 blocks (20 bytes per 32 values; the q50 rows of the
 // Q8_0 table), decoded to signed bytes on their way into LDS.
-template <int NW, bool PARTIALS, bool WST, bool Q5>
+// WNT: W rows loaded with the nontemporal bit (set when at most two M tiles
+// read each W slab, so the slab is not wanted in the L2 afterwards).
+template <int NW, bool PARTIALS, bool WST, bool Q5, bool WNT>
 __global__ void __launch_bounds__(NW * kWave)
 qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -134,7 +136,7 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         for (int q = 0; q < 4; ++q) {
             const int v = vo == kNoRead ? kNoRead : vo + 8 * q * K;
             raw.a[q] = buffer_load16(rA, v, so);
-            if constexpr (!Q5) raw.w[q] = buffer_load16(rW, v, so);
+            if constexpr (!Q5) raw.w[q] = WNT ? buffer_load16_nt(rW, v, so) : buffer_load16(rW, v, so);
         }
         if constexpr (Q5) {
             // whole blocks per lane; rows past N and blocks past K load
@@ -287,10 +289,21 @@ hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const fl
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     constexpr size_t smem = ksplit_smem_bytes<NW>();
     static_assert(smem <= 160 * 1024, "LDS budget");
-    auto kern = qgemm_ksplit_kernel<NW, PARTIALS, WST, Q5>;
+    // Q8_0 W rows stream with the nontemporal bit when at most two M tiles
+    // (which run side by side on one XCD) read each W slab, measured on
+    // MI355X: M=16, N=14336, K=4096 21.2 -> 18.9 us; M=64, N=4096: 10.9 ->
+    // 10.5 us; with four M tiles it lost (M=127, N=300: 11.3 -> 12.9 us).
+    bool wnt = false;
+    auto kern = qgemm_ksplit_kernel<NW, PARTIALS, WST, Q5, false>;
+    if constexpr (!Q5) {
+        if (m_tiles <= 2) {
+            wnt = true;
+            kern = qgemm_ksplit_kernel<NW, PARTIALS, WST, Q5, true>;
+        }
+    }
     if (smem > 64 * 1024) {
-        static std::atomic<uint64_t> lds_set{0};
-        const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)smem, lds_set);
+        static std::atomic<uint64_t> lds_set[2] = {{0}, {0}};
+        const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)smem, lds_set[wnt]);
         if (e != hipSuccess) return e;
     }
     kern<<<dim3((unsigned)total), NW * kWave, smem, stream>>>(A, AS, W, WS, C, P, M, N, K,
