@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--others", default="0,2,3", help="other workloads timed briefly ('' for none)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the qmma_t / Q5_0 / small-batch timings")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0, help="CPU oracle sample budget (0: skip)")
     ap.add_argument("--no-rotate", action="store_true", help="reuse one copy (cache-warm number)")
     ap.add_argument("--profile", action="store_true",
                     help="only launch the headline kernel (for rocprofv3 counter passes)")
@@ -214,42 +214,79 @@ def copy_calibration(torch, mib: int):
     print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 10}), flush=True)
 
 
-def cpu_baseline(ops_w: synth.Workload, budget_s: float):
-    """The oracle as it stands, on this host, on a bounded sample of the workload."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def _time_oracle(fn, budget_s: float, min_runs: int = 3):
+    """Median seconds of repeated calls of fn, for about budget_s (at least min_runs)."""
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if len(times) >= min_runs and time.perf_counter() - t_all >= budget_s:
+            break
+    return statistics.median(times), len(times), sum(times)
+
+
+def cpu_baseline(ops_w: synth.Workload, gemm_w, budget_s: float):
+    """The oracle as it stands, on this host, on bounded samples of the workloads.
+
+    Headline: full passes of the decode workload on all the oracle's threads
+    (the reported value) and on one thread.  GEMM: the first rows of the
+    prompt-size workload against the whole weight, on all threads, in int8
+    TOPS.  Quantization is outside every timed call.
+    """
     import oracle
     a32, w32 = synth.workload_f32(ops_w)
     A, AS = oracle.quantize_rows(a32)
     W, WS = oracle.quantize_rows(w32)
     del a32, w32
-    times = []
-    t_all = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        oracle.qdot_f64(A, AS, W, WS)
-        times.append(time.perf_counter() - t0)
-        if len(times) >= 3 and time.perf_counter() - t_all >= budget_s:
-            break
-    per = statistics.median(times)
+    threads = oracle.num_threads()
     wbytes = W.nbytes + WS.nbytes
-    cpu_model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {
+    per, n, tot = _time_oracle(lambda: oracle.qdot_f64(A, AS, W, WS), 0.45 * budget_s)
+    rec = {
         "value": round(wbytes / per / 1e9, 3),
         "unit": "GB/s",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": "%d full passes of %s (M=%d N=%d K=%d), median %.1f ms each, %.1f s total; "
-                  "host %s, %d CPUs in affinity"
-                  % (len(times), ops_w.name, ops_w.M, ops_w.N, ops_w.K, per * 1e3,
-                     sum(times), cpu_model or platform.processor(), len(os.sched_getaffinity(0))),
+        "sample": "%d full passes of %s (M=%d N=%d K=%d), median %.2f ms each, %.1f s total; "
+                  "host %s, %d CPUs in affinity; oracle built with '%s'"
+                  % (n, ops_w.name, ops_w.M, ops_w.N, ops_w.K, per * 1e3, tot, _cpu_model(),
+                     len(os.sched_getaffinity(0)), oracle.BUILD_FLAGS),
     }
+    oracle.set_num_threads(1)
+    try:
+        per1, n1, tot1 = _time_oracle(lambda: oracle.qdot_f64(A, AS, W, WS), 0.2 * budget_s)
+    finally:
+        oracle.set_num_threads(threads)
+    rec["one_thread"] = {"value": round(wbytes / per1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                         "sample": "%d full passes of %s, median %.1f ms each, %.1f s total"
+                                   % (n1, ops_w.name, per1 * 1e3, tot1)}
+    del A, AS, W, WS
+    if gemm_w is not None:
+        a32, w32 = synth.workload_f32(gemm_w)
+        rows = min(gemm_w.M, 32)
+        A, AS = oracle.quantize_rows(a32[:rows])
+        W, WS = oracle.quantize_rows(w32)
+        del a32, w32
+        perg, ng, totg = _time_oracle(lambda: oracle.qdot_f64(A, AS, W, WS), 0.35 * budget_s)
+        ops = 2.0 * rows * gemm_w.N * gemm_w.K
+        rec["gemm"] = {"value": round(ops / perg / 1e12, 4), "unit": "int8 TOPS", "cores": threads,
+                       "sample": "%d passes over the first %d of %d activation rows of %s "
+                                 "(N=%d K=%d), median %.1f ms each, %.1f s total"
+                                 % (ng, rows, gemm_w.M, gemm_w.name, gemm_w.N, gemm_w.K,
+                                    perg * 1e3, totg)}
+    return rec
 
 
 def main():
@@ -388,6 +425,10 @@ def main():
         sec = Operands(torch, q8, sw, rotate=not args.no_rotate)
         steps2 = max(10, args.steps // 4)
         ms2, _ = time_launches(torch, q8, sec, steps2, max(3, args.warmup // 4))
+        # and sustained: a long run of back-to-back launches (the clock
+        # settles lower under the epilogue's load)
+        steps_sus = max(60, args.steps // 2)
+        ms_sus, _ = time_launches(torch, q8, sec, steps_sus, 0)
         tops = sec.int8_ops / (ms2 * 1e-3) / 1e12
         valu_floor_us = sec.element_blocks * EPILOGUE_VALU_OPS / VALU_LANE_OPS_PER_S * 1e6
         hbm_gbs = sec.algo_bytes / (ms2 * 1e-3) / 1e9
@@ -402,9 +443,14 @@ def main():
             "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
             "rotated_copies": sec.R,
             "traffic": measured_traffic(sw.name, KERNEL_SOURCES[q8.q8_qdot_path(sw.M, sw.N, sw.K)]),
+            "sustained": {"steps": steps_sus, "us_per_launch": round(ms_sus * 1e3, 3),
+                          "int8_tops": round(sec.int8_ops / (ms_sus * 1e-3) / 1e12, 2),
+                          "frac_int8_peak": round(sec.int8_ops / (ms_sus * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                          "valu_floor_frac": round(valu_floor_us / (ms_sus * 1e3), 4)},
         }
-        log("[bench] second %s: %.3f us/launch, %.1f int8 TOPS (%.1f%% of peak), VALU floor %.1f us"
-            % (sw.name, ms2 * 1e3, tops, 100 * tops / INT8_PEAK_TOPS, valu_floor_us))
+        log("[bench] second %s: %.3f us/launch, %.1f int8 TOPS (%.1f%% of peak), VALU floor %.1f us; "
+            "sustained over %d launches %.3f us"
+            % (sw.name, ms2 * 1e3, tops, 100 * tops / INT8_PEAK_TOPS, valu_floor_us, steps_sus, ms_sus * 1e3))
         del sec
         torch.cuda.empty_cache()
 
@@ -412,7 +458,8 @@ def main():
 
     if args.cpu_seconds > 0:
         log("[bench] CPU oracle baseline (~%.0f s)" % args.cpu_seconds)
-        result["cpu_baseline"] = cpu_baseline(head_w, args.cpu_seconds)
+        gemm_w = synth.WORKLOADS[args.second] if args.second >= 0 else None
+        result["cpu_baseline"] = cpu_baseline(head_w, gemm_w, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

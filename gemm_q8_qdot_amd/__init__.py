@@ -24,8 +24,8 @@ Q8_OK = 0
 Q8_EINVAL = -1
 Q8_ENULL = -2
 Q8_EALIGN = -3
-Q8_ERANGE = -4
-Q8_ELAUNCH = -5
+Q8_ELAUNCH = -4
+Q8_ERANGE = -5
 
 # Every symbol include/q8qdot.h declares.
 EXPORTS = ("q8_qdot", "q8_qdot_stream", "q8_qmma", "q8_qdot_partials", "q8_qdot_path",

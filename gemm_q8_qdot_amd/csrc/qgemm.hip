@@ -31,8 +31,10 @@
 // column.  The activation scale of a result register's row comes from one
 // VGPR per block: lane 16 q + n of a 16-lane row holds the scale of row
 // tile_row(n, half), and the accumulate is a v_fmac_f32 whose scale operand
-// is broadcast from lane r of the row (DPP row_newbcast).  Requires
-// |WS| < 2^100 so the bias product stays finite.
+// is broadcast from lane r of the row (DPP row_newbcast).  The bias product
+// -12582912 ws_hi is finite for |WS| below about 2^104; a wave whose results
+// come out non-finite (that, or ws * p overflowing before the activation
+// scale) recomputes its tiles in the plain order (AS * WS) * p.
 //
 // Two kernels:
 //   staged  -- large M: a 16-wave workgroup owns a 128 x 224 output tile
@@ -275,9 +277,12 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     // Row of the activation-scale tile this lane holds for the DPP broadcast.
     const int as_row = mw * kTile + tile_row(lane % 16, half);
 
+    // The same seed in both modes: the debug entry issues exactly the MFMAs
+    // of the f32 path and stores D - kBias (the exact block sum) where the
+    // f32 path applies the epilogue.
     v16i bias;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bias[r] = PARTIALS ? 0 : kBias;
+    for (int r = 0; r < 16; ++r) bias[r] = kBias;
     // Opaque to the optimizer: the tile stays in 16 VGPRs instead of being
     // rebuilt from a scalar before every block.
     asm volatile("" : "+v"(bias));
@@ -287,23 +292,16 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-    // Debug entry: the int32 block sums of block s of stage st for this
-    // wave's one or two tiles, stored raw (blocks past K are skipped).
-    auto block_partials = [&](auto nt_const, const StagedStage<TN>& sg, int st, int s) {
-        constexpr int NT = decltype(nt_const)::value;
-        const int kb = st * kSB + s;
-        const v4i af = *reinterpret_cast<const v4i*>(sg.a + mw * kTile * kSeg + frag_off[s]);
-        if (kb < KB) {
+    // Debug entry: the int32 block sums of block kb for weight tile t0 + tp of
+    // this wave, from a result tile d seeded with kBias (blocks past K and
+    // the no-op before the first stage, kb < 0, are skipped).
+    auto store_partials = [&](const v16i& d, int kb, int tp) {
+        const int j = j0 + (t0 + tp) * kTile + col;
+        if (kb >= 0 && kb < KB && j < N) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const v4i wf = *reinterpret_cast<const v4i*>(sg.w + (t0 + t) * kTile * kSeg + frag_off[s]);
-                const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
-                const int j = j0 + (t0 + t) * kTile + col;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = i0 + mw * kTile + tile_row(r, half);
-                    if (i < M && j < N) P[((int64_t)i * N + j) * KB + kb] = d[r];
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + mw * kTile + tile_row(r, half);
+                if (i < M) P[((int64_t)i * N + j) * KB + kb] = d[r] - kBias;
             }
         }
     };
@@ -334,27 +332,46 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         fmac_rowbcast8<8>(a, as_blk, u);
     };
 
+    // This wave's NT tiles recomputed without the ring (no barriers): the
+    // operand fragments straight from memory, one MFMA per block with a zero
+    // seed, and acc += (AS * WS) * p per element.  Reached only when the
+    // fast epilogue's result is not finite.
+    auto exact_tiles = [&](auto nt_const, float (&a)[2][16]) {
+        constexpr int NT = decltype(nt_const)::value;
+        const v16i zero = {};
+        const int ia = i0 + mw * kTile + col;  // operand row this lane supplies
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[t][r] = 0.0f;
+        for (int kb = 0; kb < KB; ++kb) {
+            const int ko = kb * kBlock + 16 * half;
+            const v4i af = ia < M ? load16(A + (int64_t)ia * K + ko) : v4i{0, 0, 0, 0};
+            float asr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ir = i0 + mw * kTile + tile_row(r, half);
+                asr[r] = ir < M ? AS[(int64_t)ir * KB + kb] : 0.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int jw = j0 + (t0 + t) * kTile + col;
+                const v4i wf = jw < N ? load16(W + (int64_t)jw * K + ko) : v4i{0, 0, 0, 0};
+                const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, zero, 0, 0, 0);
+                const float ws = jw < N ? (WST ? WS[(int64_t)kb * N + jw] : WS[(int64_t)jw * KB + kb]) : 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) a[t][r] = fmaf(asr[r] * ws, (float)d[r], a[t][r]);
+            }
+        }
+    };
+
     // The stage loop and the stores, for a wave with NT (1 or 2) tiles: one
     // straight run of code per case (a branch per tile inside the loop makes
     // the register allocator spill).
     auto run = [&](auto nt_const) {
         constexpr int NT = decltype(nt_const)::value;
         int rs = 0;  // ring slot of stage st; stage st + 2 goes to the slot before it
-        if constexpr (PARTIALS) {
-            for (int st = 0; st < nstages; ++st) {
-                const bool ahead = st + 2 < nstages;
-                const int rs2 = rs == 0 ? kRing - 1 : rs - 1;
-                const StagedStage<TN>& sg = ring[rs];
-#pragma unroll
-                for (int s = 0; s < kSB; ++s) {
-                    fetch_slice(st + 2, rs2, s, ahead);
-                    block_partials(nt_const, sg, st, s);
-                }
-                wait_vmcnt_stage();
-                __builtin_amdgcn_s_barrier();
-                rs = rs == kRing - 1 ? 0 : rs + 1;
-            }
-        } else {
+        {
             // Software pipeline over the stage's 4 NT tile-blocks q = NT s + t
             // (block s, weight tile t): the MFMA of q is issued before the
             // epilogue of q - 1, so every MFMA runs while the previous
@@ -362,7 +379,9 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             // tiles (4 NT is even: tile-block q always uses dq[q % 2]).  The
             // last tile-block's epilogue is deferred past the stage barrier;
             // before the first stage the deferred one is an exact no-op (a
-            // zero scale pair on the bias tile, whose p is 0).
+            // zero scale pair on the bias tile, whose p is 0).  The debug
+            // entry runs this same loop and stores each result tile's block
+            // sums where the epilogue would be applied.
             v16i dq[2];
             dq[0] = bias;
             dq[1] = bias;
@@ -402,7 +421,8 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                         if (q == 0) {
                             // the deferred epilogue of the previous stage
                             // covers the fragment reads of this one
-                            epilogue(dq[1], wp_pend, as_pend, acc[NT - 1]);
+                            if constexpr (PARTIALS) store_partials(dq[1], st * kSB - 1, NT - 1);
+                            else epilogue(dq[1], wp_pend, as_pend, acc[NT - 1]);
                             dq[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf[0], bias, 0, 0, 0);
                         } else {
                             dq[q & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf[t], bias, 0, 0, 0);
@@ -419,26 +439,44 @@ qgemm_staged_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                         }
                         if (q > 0) {
                             const int sp = (q - 1) / NT, tp = (q - 1) % NT;
-                            epilogue(dq[(q - 1) & 1], ws_pair(wsv[sp][tp]), as4[sp], acc[tp]);
+                            if constexpr (PARTIALS) store_partials(dq[(q - 1) & 1], st * kSB + sp, tp);
+                            else epilogue(dq[(q - 1) & 1], ws_pair(wsv[sp][tp]), as4[sp], acc[tp]);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-                wp_pend = ws_pair(wsv[kSB - 1][NT - 1]);
-                as_pend = as4[kSB - 1];
+                if constexpr (!PARTIALS) {
+                    wp_pend = ws_pair(wsv[kSB - 1][NT - 1]);
+                    as_pend = as4[kSB - 1];
+                }
                 wait_vmcnt_stage();
                 // Bare barrier (no fence): the loads of stage st + 2 stay in flight.
                 __builtin_amdgcn_s_barrier();
                 rs = rs == kRing - 1 ? 0 : rs + 1;
             }
-            epilogue(dq[1], wp_pend, as_pend, acc[NT - 1]);
+            if constexpr (PARTIALS) {
+                store_partials(dq[1], nstages * kSB - 1, NT - 1);
+            } else {
+                epilogue(dq[1], wp_pend, as_pend, acc[NT - 1]);
+                // The fast epilogue needs |WS| below ~2^104 (its bias product
+                // -12582912 ws must be finite) and forms ws * p before the
+                // activation scale.  A wave whose results came out non-finite
+                // recomputes its tiles in the plain order (AS * WS) * p, which
+                // is finite wherever the products AS * WS and the sums are.
+                bool bad = false;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int j = j0 + (t0 + t) * kTile + col;
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = i0 + mw * kTile + tile_row(r, half);
-                    if (i < M && j < N) C[(int64_t)i * N + j] = acc[t][r];
+                    for (int r = 0; r < 16; ++r) bad |= !__builtin_isfinite(acc[t][r]);
+                if (__builtin_amdgcn_ballot_w64(bad) != 0) exact_tiles(nt_const, acc);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int j = j0 + (t0 + t) * kTile + col;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = i0 + mw * kTile + tile_row(r, half);
+                        if (i < M && j < N) C[(int64_t)i * N + j] = acc[t][r];
+                    }
                 }
             }
         }
@@ -474,10 +512,10 @@ hipError_t launch_staged(const int8_t* A, const float* AS, const int8_t* W, cons
                          float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
     // 16-byte weight-scale loads need whole stages and a 16-byte aligned WS
     // (and, transposed, rows of 4-aligned length).
+    // The debug entry (no scales) takes the mode the f32 entry takes for the
+    // same shape, so it issues the same loads and runs the same loop.
     const bool whole = (K / kBlock) % kSB == 0 && (reinterpret_cast<uintptr_t>(WS) & 15) == 0;
-    if constexpr (PARTIALS) {
-        return launch_staged_v<TN, PARTIALS, 0>(A, AS, W, WS, C, P, M, N, K, stream);
-    } else if (ws_t) {
+    if (ws_t) {
         if (whole && N % 4 == 0) return launch_staged_v<TN, PARTIALS, 3>(A, AS, W, WS, C, P, M, N, K, stream);
         return launch_staged_v<TN, PARTIALS, 2>(A, AS, W, WS, C, P, M, N, K, stream);
     } else {

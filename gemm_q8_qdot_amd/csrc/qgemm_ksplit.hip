@@ -169,16 +169,20 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         }
     };
 
+    // One seed for both modes: the debug entry issues the f32 path's MFMAs
+    // and stores D - kBias, the exact block sum.
     v16i bias;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) bias[r] = PARTIALS ? 0 : kBias;
+    for (int r = 0; r < 16; ++r) bias[r] = kBias;
     asm volatile("" : "+v"(bias));
 
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-    auto stage_and_compute = [&](const KsRaw& raw, int c) {
+    // exact: the plain-order epilogue acc += (AS * WS) * p, taken when the
+    // fast form's result is not finite (see below).
+    auto stage_and_compute = [&](const KsRaw& raw, int c, bool exact) {
         // Lanes exchange data through this wave's LDS area: keep the compiler
         // from moving LDS accesses across the write/read boundaries (the LDS
         // queue itself serves one wave's accesses in order).
@@ -229,10 +233,10 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int64_t i = i0 + tile_row(r, half);
-                        if (i < M) P[(i * N + j) * KB + b] = d[r];
+                        if (i < M) P[(i * N + j) * KB + b] = d[r] - kBias;
                     }
                 }
-            } else {
+            } else if (!exact) {
                 const float2 wp = ws_pair(wsv[t]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -246,6 +250,17 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                         acc[r] = fmaf(av[e], u, acc[r]);
                     }
                 }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(&st.as[t][8 * q + 4 * half]);
+                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * q + e;
+                        acc[r] = fmaf(av[e] * wsv[t], (float)(d[r] - kBias), acc[r]);
+                    }
+                }
             }
         }
     };
@@ -257,7 +272,26 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     for (int c = c_begin; c < c_end; ++c) {
         KsRaw r0;
         load_chunk(r0, c);
-        stage_and_compute(r0, c);
+        stage_and_compute(r0, c, false);
+    }
+    if constexpr (!PARTIALS) {
+        // The fast epilogue's bias product -12582912 ws is finite for |WS|
+        // below about 2^104, and it forms ws * p before the activation scale:
+        // a wave whose partial tile came out non-finite recomputes its chunks
+        // in the plain order (AS * WS) * p (finite wherever AS * WS and the
+        // sums are).
+        bool bad = false;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bad |= !__builtin_isfinite(acc[r]);
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            for (int c = c_begin; c < c_end; ++c) {
+                KsRaw r0;
+                load_chunk(r0, c);
+                stage_and_compute(r0, c, true);
+            }
+        }
     }
 
     if constexpr (!PARTIALS) {

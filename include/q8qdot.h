@@ -43,6 +43,17 @@
  *     buffer cannot be detected and reads or writes past it, as on the pages.
  *     A fault inside a kernel surfaces at the caller's next synchronize.
  *   - Calls are reentrant; calls on different streams may overlap.
+ *   - Numerics: int32 block sums are exact; C is within
+ *     1e-5 * sum_b |AS * WS * P| + 1e-6 of the exact sum for finite inputs
+ *     whose per-block products AS[i, b] * WS[j, b] and partial sums are
+ *     finite in f32.  The M >= 8 kernels use a 2-operation epilogue whose
+ *     bias product is finite for |WS| below about 2^104; a tile whose result
+ *     comes out non-finite is recomputed in the plain order (AS * WS) * P,
+ *     so any finite scales work.  That epilogue drops the two lowest
+ *     mantissa bits of each weight scale: at most 3.6e-7 relative for a
+ *     normal scale; for a subnormal one (below 2^-126) at most
+ *     3 * 2^-149 * |AS * P| per block, below the absolute term of the bound
+ *     unless |AS| exceeds about 10^26.
  */
 #ifndef Q8QDOT_H
 #define Q8QDOT_H
@@ -58,10 +69,10 @@ typedef enum {
     Q8_EINVAL = -1,  /* M, N or K negative, or K % 32 != 0 */
     Q8_ENULL = -2,   /* a pointer the call must dereference is NULL */
     Q8_EALIGN = -3,  /* A/W/X/Q not 16-byte aligned, or W5 or another array not 4-byte aligned */
-    Q8_ERANGE = -4,  /* an extent product overflows 64-bit byte addressing, or
+    Q8_ELAUNCH = -4, /* the HIP runtime rejected the launch (hipGetLastError) */
+    Q8_ERANGE = -5   /* an extent product overflows 64-bit byte addressing, or
                         M >= 8 with 32 * K > 2^31 - 1 (32-bit tile offsets), or
                         q8_qmma with M >= 8 and (K/32) * N * 4 > 2^31 - 1 */
-    Q8_ELAUNCH = -5  /* the HIP runtime rejected the launch (hipGetLastError) */
 } q8_status;
 
 /*
@@ -127,10 +138,12 @@ int q8_q50_partials(const int8_t *A, const uint8_t *W5, int32_t *P, int M, int N
 
 /*
  * Debug entry: P[i][j][b] = the int32 block sum of the qdot_t definition,
- * int32 [M][N][K/32] row-major.  Runs the same kernel and the same load and
- * integer-dot code as q8_qdot for this (M, N, K), stopping before the f32
- * block-scale epilogue, so each kernel's integer core can be checked bit for
- * bit.  K == 0 is an empty P: OK, nothing is launched.
+ * int32 [M][N][K/32] row-major.  Runs the kernel q8_qdot runs for this
+ * (M, N, K), with the same loads, the same integer-dot instructions and (in
+ * the GEMMs) the same software-pipelined loop and accumulator seed, and
+ * stores each block sum where q8_qdot applies the f32 block scales, so each
+ * kernel's integer core can be checked bit for bit.  K == 0 is an empty P:
+ * OK, nothing is launched.
  */
 int q8_qdot_partials(const int8_t *A, const int8_t *W, int32_t *P,
                      int M, int N, int K, void *stream);

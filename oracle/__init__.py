@@ -48,8 +48,7 @@ def build(force: bool = False) -> str:
     """Compile ``q8_oracle.c`` into ``liboracle.so`` (gcc, OpenMP)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
-               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+        cmd = BUILD_FLAGS.split() + ["-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -69,6 +68,8 @@ def _load():
             i64 = ctypes.c_int64
             lib.q8o_num_threads.restype = ctypes.c_int
             lib.q8o_num_threads.argtypes = []
+            lib.q8o_set_num_threads.restype = None
+            lib.q8o_set_num_threads.argtypes = [ctypes.c_int]
             lib.q8o_quantize_rows.restype = ctypes.c_int
             lib.q8o_quantize_rows.argtypes = [p, i64, i64, p, p]
             lib.q8o_block_partials.restype = ctypes.c_int
@@ -106,6 +107,14 @@ def _c(a, dtype) -> np.ndarray:
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(_load().q8o_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later calls (its OpenMP loops)."""
+    _load().q8o_set_num_threads(int(n))
+
+
+BUILD_FLAGS = "gcc -O2 -std=c11 -fopenmp -ffp-contract=off"
 
 
 def quantize_rows(x: np.ndarray):

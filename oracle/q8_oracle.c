@@ -55,6 +55,15 @@ int q8o_num_threads(void) {
 #endif
 }
 
+/* Set the number of threads for later calls (no effect without OpenMP). */
+void q8o_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Q8_0 quantization of `rows` f32 rows of length K (K >= 0, a multiple of 32).
  * q: int8 [rows][K]; d: f32 [rows][K/32].  Returns 0, or -1 for a bad K.

@@ -37,6 +37,23 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def _declared_status_values():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef enum\s*\{(.*?)\}\s*q8_status;", text, flags=re.S).group(1)
+    return {k: int(v) for k, v in re.findall(r"\b(Q8_[A-Z]+)\s*=\s*(-?\d+)", body)}
+
+
+def test_status_values():
+    # The five codes of the boundary contract keep their fixed values (a
+    # caller written against it reads -4 as a launch failure); the range
+    # error is this library's addition and takes the next free value.
+    vals = _declared_status_values()
+    assert vals == {"Q8_OK": 0, "Q8_EINVAL": -1, "Q8_ENULL": -2, "Q8_EALIGN": -3,
+                    "Q8_ELAUNCH": -4, "Q8_ERANGE": -5}
+    for name, v in vals.items():
+        assert getattr(q8, name) == v, name
+
+
 def test_version_and_strerror(lib):
     assert q8.q8_version() >= 100
     for st in (0, -1, -2, -3, -4, -5):

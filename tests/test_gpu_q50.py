@@ -116,3 +116,11 @@ def test_q50_extreme_codes(dev):
     WS = np.full((N, K // 32), 0.25, np.float32)
     _check(A, AS, W5, WS, dev, "extreme")
     _check(A[:1], AS[:1], W5, WS, dev, "extreme-matvec")
+    # weight scales of 2^110 / 2^126 against activation scales of their
+    # inverse: the GEMM's fast epilogue overflows and the tile is recomputed
+    # in the plain order
+    for b, e in ((1, 110), (5, 126)):
+        WS[5:30, b] = np.float32(2.0 ** e)
+        AS[:, b] = np.float32(2.0 ** -e)
+    _check(A, AS, W5, WS, dev, "huge weight scales")
+    _check(A[:1], AS[:1], W5, WS, dev, "huge weight scales (matvec)")

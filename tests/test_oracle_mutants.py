@@ -36,6 +36,8 @@ MUTANTS = {
     "q50_qh_big_endian": ("const uint32_t qh = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8) |",
                           "const uint32_t qh = (uint32_t)blk[3] | ((uint32_t)blk[2] << 8) | 0u * blk[0] |"),
     "qmma_scale_not_transposed": ("(double)WST[b * N + j]", "(double)WST[j * KB + b]"),
+    "q50_sampled_column_misindexed": ("q50_one(A, AS, W5, WS, ws_t, ii[s], jj[s], N, K, out + s, abs_terms + s);",
+                                      "q50_one(A, AS, W5, WS, ws_t, ii[s], jj[count - 1 - s], N, K, out + s, abs_terms + s);"),
     "transposed_weight_operand": ("W + j * K + b * Q8_BLOCK);\n        double s",
                                   "W + (j % 1) * K + b * Q8_BLOCK);\n        double s"),
 }

@@ -333,10 +333,19 @@ def test_q50_exact_rational_bruteforce(M, N, K, seed):
         W_scales = np.ascontiguousarray(WS.T) if ws_t else WS
         ex = brute.exact_definition_q50(A, AS, W5, W_scales, ws_t)
         out, mag = (oracle.q50_qmma_f64 if ws_t else oracle.q50_qdot_f64)(A, AS, W5, W_scales)
+        # the sampled form, at every position listed twice in a scrambled order
+        ii = np.tile(np.repeat(np.arange(M), N), 2)[::-1].copy()
+        jj = np.tile(np.tile(np.arange(N), M), 2)[::-1].copy()
+        o_at, m_at = oracle.q50_f64_at(A, AS, W5, W_scales, ws_t, ii, jj)
         for i in range(M):
             for j in range(N):
                 bound = 2.0 * KB * 2.0 ** -53 * float(mag[i, j]) + 1e-300
                 assert abs(out[i, j] - float(ex[i][j])) <= bound
+        for s in range(ii.shape[0]):
+            i, j = int(ii[s]), int(jj[s])
+            bound = 2.0 * KB * 2.0 ** -53 * float(mag[i, j]) + 1e-300
+            assert abs(o_at[s] - float(ex[i][j])) <= bound
+            assert m_at[s] == mag[i, j]
     # the pure-Python decoder and the oracle's agree value for value
     Wd = oracle.q50_decode(W5, K)
     for j in range(N):
