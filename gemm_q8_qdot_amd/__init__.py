@@ -29,6 +29,7 @@ Q8_ERANGE = -5
 
 # Every symbol include/q8qdot.h declares.
 EXPORTS = ("q8_qdot", "q8_qdot_stream", "q8_qmma", "q8_qdot_partials", "q8_qdot_path",
+           "q8_qdot_ws_size", "q8_qdot_ws", "q8_qmma_ws", "q8_qdot_ws_partials",
            "q8_q50_qdot", "q8_q50_qmma", "q8_q50_partials",
            "q8_quantize", "q8_strerror", "q8_version")
 
@@ -72,6 +73,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.q8_q50_partials.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qdot_partials.restype = ci
         lib.q8_qdot_partials.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+        for name in ("q8_qdot_ws", "q8_qmma_ws"):
+            getattr(lib, name).restype = ci
+            getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp, ctypes.c_size_t, vp]
+        lib.q8_qdot_ws_size.restype = ci
+        lib.q8_qdot_ws_size.argtypes = [ci, ci, ci, ctypes.POINTER(ctypes.c_size_t)]
+        lib.q8_qdot_ws_partials.restype = ci
+        lib.q8_qdot_ws_partials.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qdot_path.restype = ci
         lib.q8_qdot_path.argtypes = [ci, ci, ci]
         lib.q8_quantize.restype = ci
@@ -124,6 +132,17 @@ def q8_q50_qdot_raw(A: int, AS: int, W5: int, WS: int, C: int, M: int, N: int, K
     """``q8_q50_qdot`` (or, with ``ws_t``, ``q8_q50_qmma``) on raw device addresses."""
     f = load().q8_q50_qmma if ws_t else load().q8_q50_qdot
     return f(A, AS, W5, WS, C, M, N, K, stream or None)
+
+
+def q8_qdot_ws_raw(A: int, AS: int, W: int, WS: int, C: int, M: int, N: int, K: int,
+                   workspace: int, ws_bytes: int, stream: int = 0, ws_t: bool = False) -> int:
+    """``q8_qdot_ws`` (or, with ``ws_t``, ``q8_qmma_ws``) on raw device addresses."""
+    f = load().q8_qmma_ws if ws_t else load().q8_qdot_ws
+    return f(A, AS, W, WS, C, M, N, K, workspace or None, ws_bytes, stream or None)
+
+
+def q8_qdot_ws_partials_raw(A: int, W: int, P: int, M: int, N: int, K: int, stream: int = 0) -> int:
+    return load().q8_qdot_ws_partials(A, W, P, M, N, K, stream or None)
 
 
 def q8_q50_partials_raw(A: int, W5: int, P: int, M: int, N: int, K: int, stream: int = 0) -> int:
@@ -228,6 +247,71 @@ def q8_qdot_partials(A, W, P=None, stream=None):
     s = stream.cuda_stream if stream is not None else _current_stream(A.device)
     st = load().q8_qdot_partials(_ptr(A), _ptr(W), _ptr(P), M, N, K, s or None)
     _check(st, "q8_qdot_partials")
+    return P
+
+
+def q8_qdot_ws_size(M: int, N: int, K: int) -> int:
+    """Workspace bytes ``q8_qdot_ws`` / ``q8_qmma_ws`` use for this shape on the
+    current device (0: the shape does not take the split form)."""
+    n = ctypes.c_size_t(0)
+    _check(load().q8_qdot_ws_size(M, N, K, ctypes.byref(n)), "q8_qdot_ws_size")
+    return int(n.value)
+
+
+def workspace(M: int, N: int, K: int, device=None):
+    """A zero-filled uint8 device tensor of ``q8_qdot_ws_size(M, N, K)`` bytes
+    (at least one byte), for the ``*_ws`` entries."""
+    torch = _torch()
+    return torch.zeros(max(1, q8_qdot_ws_size(M, N, K)), dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+
+
+def _ws_call(A, AS, W, WS, workspace, C, stream, ws_t):
+    torch = _torch()
+    M, K = A.shape
+    N = W.shape[0]
+    KB = K // 32
+    _need(A, torch.int8, (M, K), "A")
+    _need(AS, torch.float32, (M, KB), "AS")
+    _need(W, torch.int8, (N, K), "W")
+    _need(WS, torch.float32, (KB, N) if ws_t else (N, KB), "WST" if ws_t else "WS")
+    _need(workspace, torch.uint8, (workspace.numel(),), "workspace")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _need(C, torch.float32, (M, N), "C")
+    s = stream.cuda_stream if stream is not None else _current_stream(A.device)
+    f = load().q8_qmma_ws if ws_t else load().q8_qdot_ws
+    st = f(_ptr(A), _ptr(AS), _ptr(W), _ptr(WS), _ptr(C), M, N, K, _ptr(workspace),
+           workspace.numel(), s or None)
+    _check(st, "q8_qmma_ws" if ws_t else "q8_qdot_ws")
+    return C
+
+
+def q8_qdot_ws(A, AS, W, WS, workspace, C=None, stream=None):
+    """:func:`q8_qdot` with a caller workspace (a zero-filled uint8 tensor, see
+    :func:`workspace`); shapes with few output tiles split the contraction
+    across workgroups."""
+    return _ws_call(A, AS, W, WS, workspace, C, stream, False)
+
+
+def q8_qmma_ws(A, AS, W, WST, workspace, C=None, stream=None):
+    """:func:`q8_qmma` with a caller workspace (see :func:`q8_qdot_ws`)."""
+    return _ws_call(A, AS, W, WST, workspace, C, stream, True)
+
+
+def q8_qdot_ws_partials(A, W, P=None, stream=None):
+    """Per-block int32 partials from the kernel ``q8_qdot_ws`` uses for the shape."""
+    torch = _torch()
+    M, K = A.shape
+    N = W.shape[0]
+    _need(A, torch.int8, (M, K), "A")
+    _need(W, torch.int8, (N, K), "W")
+    if P is None:
+        P = torch.empty((M, N, K // 32), dtype=torch.int32, device=A.device)
+    _need(P, torch.int32, (M, N, K // 32), "P")
+    s = stream.cuda_stream if stream is not None else _current_stream(A.device)
+    st = load().q8_qdot_ws_partials(_ptr(A), _ptr(W), _ptr(P), M, N, K, s or None)
+    _check(st, "q8_qdot_ws_partials")
     return P
 
 

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libq8qdot.so")
 
 SOURCES = ("q8qdot_api.hip", "matvec.hip", "matvec_q50.hip", "qgemm.hip",
-           "qgemm_ksplit.hip", "quantize.hip")
+           "qgemm_ksplit.hip", "qgemm_splitk.hip", "quantize.hip")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are disabled for every device pass; hipcc's host

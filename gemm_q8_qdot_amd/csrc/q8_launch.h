@@ -62,6 +62,15 @@ hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W
                                float* C, int32_t* P, int M, int N, int K, bool ws_t,
                                hipStream_t stream);
 
+// M >= 8 with too few 64 x 64 output tiles to fill the chip: the contraction
+// split into S slices of slice_blocks blocks across workgroups, reduced in a
+// caller workspace of ws_bytes (zero-filled; left zero-filled).  false when
+// the shape does not take this form.
+bool splitk_plan(int M, int N, int K, int* S, int* slice_blocks, size_t* ws_bytes);
+hipError_t launch_qgemm_splitk(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                               float* C, int32_t* P, int M, int N, int K, bool ws_t, int S,
+                               int slice_blocks, void* workspace, hipStream_t stream);
+
 // Q5_0 weights (W5: 20 bytes per 32 values): one-row matvec for M < 8 with
 // K <= 16 Ki values; otherwise the K-split MFMA GEMM decoding into LDS.
 bool matvec_q50_fits(int K);

@@ -32,9 +32,13 @@ int check_range(int64_t M, int64_t N, int64_t K, bool partials) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ELAUNCH; }
 
-// ws_t: WS is the qmma_t form, stored transposed [K/32][N].
+// ws_t: WS is the qmma_t form, stored transposed [K/32][N].  split: the
+// workspace entries -- shapes with few output tiles take the split-K GEMM
+// when `workspace` holds at least the bytes it needs (the debug entry needs
+// none and passes split with a null workspace).
 int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS, float* C,
-             int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
+             int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream,
+             bool split = false, void* workspace = nullptr, size_t ws_bytes = 0) {
     int st = check_shape(M, N, K);
     if (st != Q8_OK) return st;
     st = check_range(M, N, K, P != nullptr);
@@ -59,6 +63,14 @@ int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
         if (!aligned(P, 4)) return Q8_EALIGN;
     } else if (!aligned(AS, 4) || !aligned(WS, 4) || !aligned(C, 4)) {
         return Q8_EALIGN;
+    }
+    if (split && M > kMatvecMaxM && q8::qgemm_variant(M, N, K) == 1) {
+        int S = 0, sb = 0;
+        size_t need = 0;
+        if (q8::splitk_plan(M, N, K, &S, &sb, &need) &&
+            (partials || (workspace != nullptr && ws_bytes >= need && aligned(workspace, 16))))
+            return status_of(q8::launch_qgemm_splitk(A, AS, W, WS, C, P, M, N, K, ws_t, S, sb,
+                                                     workspace, stream));
     }
     hipError_t e = M <= kMatvecMaxM
                        ? q8::launch_matvec(A, AS, W, WS, C, P, M, N, K, ws_t, stream)
@@ -92,6 +104,47 @@ Q8_API int q8_qdot_partials(const int8_t* A, const int8_t* W, int32_t* P, int M,
         return Q8_ENULL;
     }
     return run_qdot(A, nullptr, W, nullptr, nullptr, P, M, N, K, false, static_cast<hipStream_t>(stream));
+}
+
+Q8_API int q8_qdot_ws_size(int M, int N, int K, size_t* bytes) {
+    if (bytes == nullptr) return Q8_ENULL;
+    *bytes = 0;
+    int st = check_shape(M, N, K);
+    if (st != Q8_OK) return st;
+    st = check_range(M, N, K, false);
+    if (st != Q8_OK) return st;
+    if (M > kMatvecMaxM && K > 0 && N > 0 && q8::qgemm_variant(M, N, K) == 1) {
+        int S = 0, sb = 0;
+        size_t need = 0;
+        if (q8::splitk_plan(M, N, K, &S, &sb, &need)) *bytes = need;
+    }
+    return Q8_OK;
+}
+
+Q8_API int q8_qdot_ws(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                      float* C, int M, int N, int K, void* workspace, size_t ws_bytes,
+                      void* stream) {
+    return run_qdot(A, AS, W, WS, C, nullptr, M, N, K, false, static_cast<hipStream_t>(stream),
+                    true, workspace, ws_bytes);
+}
+
+Q8_API int q8_qmma_ws(const int8_t* A, const float* AS, const int8_t* W, const float* WST,
+                      float* C, int M, int N, int K, void* workspace, size_t ws_bytes,
+                      void* stream) {
+    return run_qdot(A, AS, W, WST, C, nullptr, M, N, K, true, static_cast<hipStream_t>(stream),
+                    true, workspace, ws_bytes);
+}
+
+Q8_API int q8_qdot_ws_partials(const int8_t* A, const int8_t* W, int32_t* P, int M, int N, int K,
+                               void* stream) {
+    if (P == nullptr) {
+        int st = check_shape(M, N, K);
+        if (st != Q8_OK) return st;
+        if (M == 0 || N == 0 || K == 0) return Q8_OK;
+        return Q8_ENULL;
+    }
+    return run_qdot(A, nullptr, W, nullptr, nullptr, P, M, N, K, false,
+                    static_cast<hipStream_t>(stream), true);
 }
 
 // Q5_0 weights: W5 is [N][K/32 * 20] bytes, 4-byte aligned (dword loads).

@@ -10,8 +10,8 @@
 // Why this shape: with M = 64 and N = 4096 there are only 2 x 128 output
 // tiles of 32 x 32, so a tile per wave leaves most SIMDs idle and makes each
 // wave walk all K/32 blocks serially.  Here a workgroup of NW waves owns one
-// tile and wave w takes a contiguous range of chunks of four Q8_0 blocks
-// (128 k).  Per chunk a wave
+// tile and wave w takes the chunks of four Q8_0 blocks (128 k) numbered
+// w, w + NW, w + 2 NW, ...  Per chunk a wave
 //   - loads the tile's 32 A rows and 32 W rows, 128 contiguous bytes of each
 //     (eight lanes per row, eight rows per 16-byte load instruction: the
 //     MFMA operand layout itself would touch 32 rows per instruction, which
@@ -21,15 +21,19 @@
 //     reads are bank-conflict-free) and reads them back in MFMA layout: an
 //     exchange inside one wave, ordered by the LDS queue of that wave;
 //   - per block one v_mfma_i32_32x32x32_i8 (one Q8_0 block) seeded with the
-//     f32 bias pattern, then the 2-op f32 epilogue of ws_pair.
-// Sixteen waves per workgroup (four per SIMD) hide the load latency; a
-// register double-buffered form (each wave's next chunk loaded while the
-// current one is computed) needs more VGPRs than four waves per SIMD allow,
-// spilled, and measured 2.4x slower on MI355X.  At the end the NW partial
-// tiles are summed in LDS in wave order (a fixed order: the result is
-// deterministic) and stored.  Tiles sharing a W slab
-// (the M tiles of one N tile) get consecutive launch slots of one XCD so the
-// slab is read from HBM once.
+//     f32 bias pattern, then the 2-op f32 epilogue of ws_pair, the
+//     activation scale broadcast by DPP from one VGPR per chunk (as in the
+//     staged GEMM) instead of sixteen LDS reads per block.
+// Sixteen waves per workgroup (four per SIMD).  Measured on MI355X (M=64,
+// N=4096, K=4096): each compute unit spends about 2 us bringing in its
+// 256 KB and about 3 us in the epilogue; keeping two chunks in flight per
+// wave (a VGPR double buffer, which fits once the wave index is scalar)
+// measured 10.1-10.4 us against 10.2-10.7 us, eight waves with four chunks
+// in flight 12.7 us, so one chunk at a time is kept.  At the end the NW
+// partial tiles are summed in LDS in wave order (a fixed order: the result
+// is deterministic) and stored.  Tiles sharing a W slab (the M tiles of one
+// N tile) get consecutive launch slots of one XCD so the slab is read from
+// HBM once.
 #include "q8_device.h"
 #include "q8_launch.h"
 
@@ -48,7 +52,7 @@ constexpr int kKsSeg = kKsBlocks * kBlock;  // 128 bytes of a row per chunk
 struct KsStage {
     int8_t a[kTile * kKsSeg];       // [row][8 chunks of 16 B], swizzled
     int8_t w[kTile * kKsSeg];
-    float as[kKsBlocks][kTile];     // [block][A row]
+    float as[kTile][kKsBlocks];     // [A row][block]
     float ws[kTile][kKsBlocks];     // [W row][block]
 };
 
@@ -86,7 +90,9 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     int m_tiles, int tiles_total) {
     extern __shared__ __align__(16) int8_t ks_smem[];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
+    // wave-uniform (readfirstlane): the chunk offsets derived from it go in
+    // scalar registers (else every buffer load sits in a readfirstlane loop)
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     // The 8 XCDs take workgroups round-robin: consecutive tiles (the M tiles
     // of one N tile) go to consecutive slots of one XCD.
     int tile = blockIdx.x;
@@ -123,6 +129,7 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     // ---- MFMA-side lane roles
     const int half = lane / 32;
     const int r32 = lane & 31;
+    const int as_row = tile_row(lane % 16, half);  // activation row whose scales this lane holds
     int frag_off[kKsBlocks];  // logical chunk 2 t + half of row r32
 #pragma unroll
     for (int t = 0; t < kKsBlocks; ++t) frag_off[t] = r32 * kKsSeg + 16 * ((2 * t + half) ^ swz(r32));
@@ -211,15 +218,22 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         if constexpr (!PARTIALS) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                st.as[sblk][16 * k + srow] = raw.as[k];
+                st.as[16 * k + srow][sblk] = raw.as[k];
                 st.ws[16 * k + srow][sblk] = raw.ws[k];
             }
         }
         asm volatile("" ::: "memory");
         const int kb0 = c * kKsBlocks;
         float4 ws4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if constexpr (!PARTIALS) ws4 = *reinterpret_cast<const float4*>(&st.ws[r32][0]);
+        float4 as4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if constexpr (!PARTIALS) {
+            ws4 = *reinterpret_cast<const float4*>(&st.ws[r32][0]);
+            // the chunk's four scales of the activation row this lane serves
+            // to its 16-lane row (see fmac_rowbcast8)
+            as4 = *reinterpret_cast<const float4*>(&st.as[as_row][0]);
+        }
         const float wsv[4] = {ws4.x, ws4.y, ws4.z, ws4.w};
+        const float asv[4] = {as4.x, as4.y, as4.z, as4.w};
 #pragma unroll
         for (int t = 0; t < kKsBlocks; ++t) {
             const int b = kb0 + t;
@@ -237,42 +251,36 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     }
                 }
             } else if (!exact) {
+                // acc[r] += AS[row r] * round(ws_hi * p[r]), the activation
+                // scale broadcast from lane r of the 16-lane row (DPP)
                 const float2 wp = ws_pair(wsv[t]);
+                float u[16];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // rows 8q + 4 half + 0..3 of the tile: one 16-byte LDS read
-                    const float4 a4 = *reinterpret_cast<const float4*>(&st.as[t][8 * q + 4 * half]);
-                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+                for (int r = 0; r < 8; ++r) u[r] = fmaf(wp.x, __int_as_float(d[r]), wp.y);
+                fmac_rowbcast8<0>(acc, asv[t], u);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * q + e;
-                        const float u = fmaf(wp.x, __int_as_float(d[r]), wp.y);
-                        acc[r] = fmaf(av[e], u, acc[r]);
-                    }
-                }
+                for (int r = 8; r < 16; ++r) u[r] = fmaf(wp.x, __int_as_float(d[r]), wp.y);
+                fmac_rowbcast8<8>(acc, asv[t], u);
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 a4 = *reinterpret_cast<const float4*>(&st.as[t][8 * q + 4 * half]);
-                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * q + e;
-                        acc[r] = fmaf(av[e] * wsv[t], (float)(d[r] - kBias), acc[r]);
-                    }
-                }
+                for (int r = 0; r < 16; ++r)
+                    acc[r] = fmaf(st.as[tile_row(r, half)][t] * wsv[t], (float)(d[r] - kBias), acc[r]);
             }
         }
     };
 
     const int nchunks = (KB + kKsBlocks - 1) / kKsBlocks;
-    const int per_wave = (nchunks + NW - 1) / NW;
-    const int c_begin = wv * per_wave;
-    const int c_end = min(c_begin + per_wave, nchunks);
-    for (int c = c_begin; c < c_end; ++c) {
+    // Wave w takes chunks w, w + NW, w + 2 NW, ...: at any moment the waves
+    // of a workgroup read consecutive 128-byte segments of their rows
+    // (measured against contiguous ranges per wave: M=32, N=4096, K=14336
+    // 35.1 -> 30.6 us, M=127, N=300, K=4160 11.9 -> 10.5 us, the M=64,
+    // N=4096, K=4096 workload unchanged within noise).
+    const int n_mine = wv < nchunks ? (nchunks - wv + NW - 1) / NW : 0;
+    auto chunk_of = [&](int n) { return wv + NW * n; };
+    for (int n = 0; n < n_mine; ++n) {
         KsRaw r0;
-        load_chunk(r0, c);
-        stage_and_compute(r0, c, false);
+        load_chunk(r0, chunk_of(n));
+        stage_and_compute(r0, chunk_of(n), false);
     }
     if constexpr (!PARTIALS) {
         // The fast epilogue's bias product -12582912 ws is finite for |WS|
@@ -286,10 +294,10 @@ qgemm_ksplit_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         if (__builtin_amdgcn_ballot_w64(bad) != 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-            for (int c = c_begin; c < c_end; ++c) {
+            for (int n = 0; n < n_mine; ++n) {
                 KsRaw r0;
-                load_chunk(r0, c);
-                stage_and_compute(r0, c, true);
+                load_chunk(r0, chunk_of(n));
+                stage_and_compute(r0, chunk_of(n), true);
             }
         }
     }

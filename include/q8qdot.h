@@ -58,6 +58,7 @@
 #ifndef Q8QDOT_H
 #define Q8QDOT_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -147,6 +148,42 @@ int q8_q50_partials(const int8_t *A, const uint8_t *W5, int32_t *P, int M, int N
  */
 int q8_qdot_partials(const int8_t *A, const int8_t *W, int32_t *P,
                      int M, int N, int K, void *stream);
+
+/*
+ * The same contractions with a caller workspace (qdot_t / qmma_t as for
+ * q8_qdot_stream and q8_qmma; "Phobos Language Spec", section "Quantized
+ * built-ins", Q8_0 table).  For M >= 8 shapes whose 64 x 64 output tiles are
+ * too few to occupy the GPU (for example M = 64, N = 4096), the contraction
+ * is split into slices of K/32 blocks across workgroups; each writes its
+ * partial f32 tile to the workspace and the last of a tile's workgroups to
+ * finish adds the partial tiles in slice order (so the result does not
+ * depend on the order in which they finish) and stores C.
+ *
+ *   q8_qdot_ws_size: *bytes = the workspace the split form needs for this
+ *     shape on the current device, or 0 when the shape does not take it.
+ *     Q8_ENULL if bytes is NULL; shape errors as for q8_qdot.
+ *   q8_qdot_ws / q8_qmma_ws: workspace is a device pointer owned by the
+ *     caller, 16-byte aligned, of ws_bytes bytes.  Its first 4096 bytes hold
+ *     one counter per output tile and must be ZERO-FILLED before the first
+ *     use; the kernel resets every counter it used, so they are zero again
+ *     after each call, and one workspace serves calls of any shape in turn.
+ *     The rest holds partial tiles (no initial value needed).  With a
+ *     workspace of at least q8_qdot_ws_size bytes the shape takes the split
+ *     form; with less (or NULL) the call is exactly q8_qdot_stream /
+ *     q8_qmma.  Calls that share a workspace must not overlap (use one
+ *     workspace per stream).  Everything else as for q8_qdot_stream /
+ *     q8_qmma.
+ *   q8_qdot_ws_partials: the int32 block sums of the kernel q8_qdot_ws runs
+ *     for this shape (given a sufficient workspace), as q8_qdot_partials
+ *     describes; it needs no workspace.
+ */
+int q8_qdot_ws_size(int M, int N, int K, size_t *bytes);
+int q8_qdot_ws(const int8_t *A, const float *AS, const int8_t *W, const float *WS,
+               float *C, int M, int N, int K, void *workspace, size_t ws_bytes, void *stream);
+int q8_qmma_ws(const int8_t *A, const float *AS, const int8_t *W, const float *WST,
+               float *C, int M, int N, int K, void *workspace, size_t ws_bytes, void *stream);
+int q8_qdot_ws_partials(const int8_t *A, const int8_t *W, int32_t *P, int M, int N, int K,
+                        void *stream);
 
 /*
  * The kernel a shape dispatches to: 0 = wave64 matvec (M < 8: with K <=
