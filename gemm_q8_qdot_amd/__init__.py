@@ -29,7 +29,7 @@ Q8_ERANGE = -5
 
 # Every symbol include/q8qdot.h declares.
 EXPORTS = ("q8_qdot", "q8_qdot_stream", "q8_qmma", "q8_qdot_partials", "q8_qdot_path",
-           "q8_qdot_ws_size", "q8_qdot_ws", "q8_qmma_ws", "q8_qdot_ws_partials",
+           "q8_qdot_ws_size", "q8_qdot_ws", "q8_qmma_ws", "q8_qdot_ws_partials", "q8_qdot_noalloc",
            "q8_q50_qdot", "q8_q50_qmma", "q8_q50_partials",
            "q8_quantize", "q8_strerror", "q8_version")
 
@@ -76,6 +76,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         for name in ("q8_qdot_ws", "q8_qmma_ws"):
             getattr(lib, name).restype = ci
             getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp, ctypes.c_size_t, vp]
+        lib.q8_qdot_noalloc.restype = ci
+        lib.q8_qdot_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qdot_ws_size.restype = ci
         lib.q8_qdot_ws_size.argtypes = [ci, ci, ci, ctypes.POINTER(ctypes.c_size_t)]
         lib.q8_qdot_ws_partials.restype = ci
@@ -139,6 +141,12 @@ def q8_qdot_ws_raw(A: int, AS: int, W: int, WS: int, C: int, M: int, N: int, K: 
     """``q8_qdot_ws`` (or, with ``ws_t``, ``q8_qmma_ws``) on raw device addresses."""
     f = load().q8_qmma_ws if ws_t else load().q8_qdot_ws
     return f(A, AS, W, WS, C, M, N, K, workspace or None, ws_bytes, stream or None)
+
+
+def q8_qdot_noalloc_raw(A: int, AS: int, W: int, WS: int, C: int, M: int, N: int, K: int,
+                        stream: int = 0) -> int:
+    """``q8_qdot_noalloc`` (the split form in the library's static scratch) on raw addresses."""
+    return load().q8_qdot_noalloc(A, AS, W, WS, C, M, N, K, stream or None)
 
 
 def q8_qdot_ws_partials_raw(A: int, W: int, P: int, M: int, N: int, K: int, stream: int = 0) -> int:

@@ -70,6 +70,13 @@ bool splitk_plan(int M, int N, int K, int* S, int* slice_blocks, size_t* ws_byte
 hipError_t launch_qgemm_splitk(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                                float* C, int32_t* P, int M, int N, int K, bool ws_t, int S,
                                int slice_blocks, void* workspace, hipStream_t stream);
+// The same with the library's file-scope scratch array as the workspace (no
+// allocation); splitk_scratch_capacity() is the largest workspace it stands
+// for.  Calls that overlap on one GPU race on it.
+size_t splitk_scratch_capacity();
+hipError_t launch_qgemm_splitk_scratch(const int8_t* A, const float* AS, const int8_t* W,
+                                       const float* WS, float* C, int M, int N, int K, bool ws_t,
+                                       int S, int slice_blocks, hipStream_t stream);
 
 // Q5_0 weights (W5: 20 bytes per 32 values): one-row matvec for M < 8 with
 // K <= 16 Ki values; otherwise the K-split MFMA GEMM decoding into LDS.

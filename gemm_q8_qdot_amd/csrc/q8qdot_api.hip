@@ -147,6 +147,29 @@ Q8_API int q8_qdot_ws_partials(const int8_t* A, const int8_t* W, int32_t* P, int
                     static_cast<hipStream_t>(stream), true);
 }
 
+// The no-allocation variant of q8_qdot_ws: the split form's workspace is
+// the library's static scratch array; other shapes run exactly q8_qdot_stream.
+Q8_API int q8_qdot_noalloc(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                           float* C, int M, int N, int K, void* stream) {
+    int st = check_shape(M, N, K);
+    if (st != Q8_OK) return st;
+    st = check_range(M, N, K, false);
+    if (st != Q8_OK) return st;
+    int S = 0, sb = 0;
+    size_t need = 0;
+    const bool split = M > kMatvecMaxM && N > 0 && K > 0 && q8::qgemm_variant(M, N, K) == 1 &&
+                       q8::splitk_plan(M, N, K, &S, &sb, &need);
+    if (!split)
+        return run_qdot(A, AS, W, WS, C, nullptr, M, N, K, false, static_cast<hipStream_t>(stream));
+    if (need > q8::splitk_scratch_capacity()) return Q8_ERANGE;
+    if ((int64_t)K * 32 > INT32_MAX) return Q8_ERANGE;
+    if (A == nullptr || W == nullptr || AS == nullptr || WS == nullptr || C == nullptr) return Q8_ENULL;
+    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(AS, 4) || !aligned(WS, 4) || !aligned(C, 4))
+        return Q8_EALIGN;
+    return status_of(q8::launch_qgemm_splitk_scratch(A, AS, W, WS, C, M, N, K, false, S, sb,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 // Q5_0 weights: W5 is [N][K/32 * 20] bytes, 4-byte aligned (dword loads).
 static int run_q50(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS, float* C,
             int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
@@ -222,7 +245,8 @@ Q8_API const char* q8_strerror(int status) {
         case Q8_EINVAL: return "invalid shape: M, N, K must be >= 0 and K a multiple of 32";
         case Q8_ENULL: return "null pointer for an operand the call must dereference";
         case Q8_EALIGN: return "misaligned pointer: A, W, X, Q need 16 bytes, Q5_0 weights and f32/int32 arrays 4";
-        case Q8_ERANGE: return "shape out of range: an extent product overflows 64-bit addressing, or a GEMM offset 32 bits";
+        case Q8_ERANGE: return "shape out of range: an extent product overflows 64-bit addressing, a GEMM offset 32 bits, "
+                               "or (q8_qdot_noalloc) the split form needs more than its 4 MiB static scratch";
         case Q8_ELAUNCH: return "HIP runtime rejected the kernel launch";
         default: return "unknown status";
     }

@@ -72,15 +72,22 @@ static_assert(kSkSmem <= 160 * 1024, "LDS budget");
 static_assert((size_t)kSkWaves * 16 * kWave * sizeof(float) <= kSkSmem, "reduction area");
 
 // WST: weight scales stored [K/32][N] (qmma_t).  S > 1: cnt (one counter per
-// tile) and part (tiles x S partial tiles) are the workspace.
+// tile) and part (tiles x S partial tiles) are the workspace; cnt_clear (or
+// null) is a counter area this kernel zero-fills for a later call.
 template <bool PARTIALS, bool WST>
 __global__ void __launch_bounds__(kSkThreads, 1)
 qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
                     float* __restrict__ C, int32_t* __restrict__ P, int M, int N, int K,
                     int tiles_m, int S, int slice_blocks, float* __restrict__ part,
-                    unsigned* __restrict__ cnt) {
+                    unsigned* __restrict__ cnt, unsigned* __restrict__ cnt_clear) {
     extern __shared__ __align__(16) unsigned char sk_smem[];
+    // The no-allocation entry's next call counts in the other counter area:
+    // zero it now (this call does not use it).
+    if (cnt_clear != nullptr && threadIdx.x < kWave) {
+        for (int k = blockIdx.x * kWave + threadIdx.x; k < kSkMaxTiles; k += gridDim.x * kWave)
+            __hip_atomic_store(&cnt_clear[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     SkStage* ring = reinterpret_cast<SkStage*>(sk_smem);
     __shared__ int last_flag;
 
@@ -369,27 +376,84 @@ bool splitk_plan(int M, int N, int K, int* S_out, int* slice_blocks_out, size_t*
     return true;
 }
 
-hipError_t launch_qgemm_splitk(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
-                               float* C, int32_t* P, int M, int N, int K, bool ws_t, int S,
-                               int slice_blocks, void* workspace, hipStream_t stream) {
+namespace {
+
+hipError_t launch_splitk(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                         float* C, int32_t* P, int M, int N, int K, bool ws_t, int S,
+                         int slice_blocks, unsigned* cnt, float* part, unsigned* cnt_clear,
+                         hipStream_t stream) {
     const int64_t tiles_m = ((int64_t)M + kSkM - 1) / kSkM;
     const int64_t tiles_n = ((int64_t)N + kSkN - 1) / kSkN;
     const int64_t total = tiles_m * tiles_n * S;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    unsigned* cnt = static_cast<unsigned*>(workspace);
-    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkCounterBytes);
     auto launch = [&](auto kern) -> hipError_t {
         static std::atomic<uint64_t> lds_set[2][2] = {{{0}, {0}}, {{0}, {0}}};
         const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)kSkSmem,
                                              lds_set[P != nullptr][ws_t]);
         if (e != hipSuccess) return e;
         kern<<<dim3((unsigned)total), kSkThreads, kSkSmem, stream>>>(
-            A, AS, W, WS, C, P, M, N, K, (int)tiles_m, S, slice_blocks, part, cnt);
+            A, AS, W, WS, C, P, M, N, K, (int)tiles_m, S, slice_blocks, part, cnt, cnt_clear);
         return hipGetLastError();
     };
     if (P != nullptr) return launch(qgemm_splitk_kernel<true, false>);
     if (ws_t) return launch(qgemm_splitk_kernel<false, true>);
     return launch(qgemm_splitk_kernel<false, false>);
+}
+
+// ---- The no-allocation form: the workspace is this file-scope device
+// array (one copy per GPU, alive until the process ends): two counter areas
+// used alternately (each call zero-fills the one the next call counts in,
+// besides resetting its own counters), then the partial tiles.  With one
+// workgroup per compute unit the split form never needs more than
+// (compute units) x 16 KiB of partial tiles: 4 MiB on MI355X.
+constexpr size_t kSkScratchParts = (size_t)4 << 20;
+constexpr size_t kSkScratchBytes = 2 * kSkCounterBytes + kSkScratchParts;
+static __device__ __align__(256) unsigned char scratch[kSkScratchBytes];
+
+// The scratch array's device address on the current device, looked up once
+// per device (with that device current) and kept; null if the lookup fails.
+// Host code must use this address: the array's own name is a host-side
+// stand-in, not a device address.
+unsigned char* scratch_on_device() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<unsigned char*> addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    unsigned char* p = addr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    addr[dev].store(static_cast<unsigned char*>(q), std::memory_order_release);
+    return static_cast<unsigned char*>(q);
+}
+
+}  // namespace
+
+hipError_t launch_qgemm_splitk(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                               float* C, int32_t* P, int M, int N, int K, bool ws_t, int S,
+                               int slice_blocks, void* workspace, hipStream_t stream) {
+    unsigned* cnt = static_cast<unsigned*>(workspace);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkCounterBytes);
+    return launch_splitk(A, AS, W, WS, C, P, M, N, K, ws_t, S, slice_blocks, cnt, part, nullptr,
+                         stream);
+}
+
+size_t splitk_scratch_capacity() { return kSkCounterBytes + kSkScratchParts; }
+
+hipError_t launch_qgemm_splitk_scratch(const int8_t* A, const float* AS, const int8_t* W,
+                                       const float* WS, float* C, int M, int N, int K, bool ws_t,
+                                       int S, int slice_blocks, hipStream_t stream) {
+    unsigned char* base = scratch_on_device();
+    if (base == nullptr) return hipErrorInvalidSymbol;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    static std::atomic<uint64_t> epoch[64];
+    const uint64_t e = epoch[dev].fetch_add(1, std::memory_order_relaxed);
+    unsigned* cnt = reinterpret_cast<unsigned*>(base + (e & 1) * kSkCounterBytes);
+    unsigned* clear = reinterpret_cast<unsigned*>(base + ((e + 1) & 1) * kSkCounterBytes);
+    float* part = reinterpret_cast<float*>(base + 2 * kSkCounterBytes);
+    return launch_splitk(A, AS, W, WS, C, nullptr, M, N, K, ws_t, S, slice_blocks, cnt, part,
+                         clear, stream);
 }
 
 }  // namespace q8

@@ -73,7 +73,9 @@ typedef enum {
     Q8_ELAUNCH = -4, /* the HIP runtime rejected the launch (hipGetLastError) */
     Q8_ERANGE = -5   /* an extent product overflows 64-bit byte addressing, or
                         M >= 8 with 32 * K > 2^31 - 1 (32-bit tile offsets), or
-                        q8_qmma with M >= 8 and (K/32) * N * 4 > 2^31 - 1 */
+                        q8_qmma with M >= 8 and (K/32) * N * 4 > 2^31 - 1, or
+                        q8_qdot_noalloc on a shape whose split form needs
+                        more than its static scratch */
 } q8_status;
 
 /*
@@ -184,6 +186,24 @@ int q8_qmma_ws(const int8_t *A, const float *AS, const int8_t *W, const float *W
                float *C, int M, int N, int K, void *workspace, size_t ws_bytes, void *stream);
 int q8_qdot_ws_partials(const int8_t *A, const int8_t *W, int32_t *P, int M, int N, int K,
                         void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): q8_qdot_ws without
+ * a workspace argument.  Where q8_qdot_ws would split the contraction, the
+ * workspace is a static device array inside the library (one per GPU, alive
+ * until the process ends): 4 MiB of partial tiles plus 8 KiB of tile
+ * counters, enough for every shape on a GPU of up to 256 compute units; a
+ * shape that would need more returns Q8_ERANGE (nothing is enqueued).  Every
+ * other shape runs exactly q8_qdot_stream.  The call allocates nothing and
+ * needs no set-up; it finds its counters at zero (each call resets the
+ * counters it used and zero-fills those the next call will use).  All calls
+ * on one GPU share the array: calls that overlap on one GPU (different
+ * streams, or threads) race and may return wrong results; serialize them.
+ * Arguments, layout, ownership and the other errors as for q8_qdot_stream.
+ */
+int q8_qdot_noalloc(const int8_t *A, const float *AS, const int8_t *W, const float *WS,
+                    float *C, int M, int N, int K, void *stream);
 
 /*
  * The kernel a shape dispatches to: 0 = wave64 matvec (M < 8: with K <=
