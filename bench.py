@@ -19,6 +19,7 @@ The GEMMs are timed last.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import platform
@@ -70,9 +71,10 @@ def parse():
 class Operands:
     """R device copies of (A, AS, W, WS, C) for one workload, quantized on the GPU.
 
-    ``kind``: "qdot" (W int8, WS [N, K/32]), "qmma" (the same weights, scales
-    stored [K/32, N]) or "q50" (W as Q5_0 blocks, 20 bytes per 32 values,
-    seeded uniform codes; scales from the Q8_0 quantization of the weights).
+    ``kind``: "qdot" (W int8, WS [N, K/32]), "qdotws" (the same through the
+    workspace entry), "qmma" (the same weights, scales stored [K/32, N]) or
+    "q50" (W as Q5_0 blocks, 20 bytes per 32 values, seeded uniform codes;
+    scales from the Q8_0 quantization of the weights).
     """
 
     def __init__(self, torch, q8, w: synth.Workload, rotate: bool, kind: str = "qdot"):
@@ -108,28 +110,68 @@ class Operands:
         self.element_blocks = w.M * w.N * w.KB
 
 
+def settle_copies(torch, ops: Operands, first: int):
+    """Read every byte of every rotated copy once, with a plain torch reduction (max).
+
+    Creating the copies leaves up to the last-level cache's size of them
+    dirty in that cache; without this pass, the first timed launches would
+    also pay for writing those lines back to HBM.  The copies are read in
+    the order first, first + 1, ..., wrapping round, so the ones read last
+    are those the warmup launches use (copies 0 .. first - 1): the timed
+    launches, which start at copy `first`, find nothing of theirs cached.
+    Not a step of the path: no library call is made.
+    """
+    R = len(ops.copies)
+    acc = []
+    for r in range(R):
+        for t in ops.copies[(first + r) % R][:4]:
+            acc.append(t.view(torch.uint8).max())
+    torch.cuda.synchronize()
+    del acc
+
+
 def time_launches(torch, q8, ops: Operands, steps: int, warmup: int):
-    """Warm up, then time exactly `steps` launches between two HIP events."""
+    """Warm up, then time exactly `steps` launches between two HIP events.
+
+    Launch k (warmup and timed alike, k = 0, 1, ...) reads rotated copy
+    k mod R, so a timed launch never re-reads a copy a warmup launch just
+    read unless there are fewer copies than launches.  The host's garbage
+    collector is held off while launches are issued.
+    """
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     cps = ops.copies
     w = ops.w
-    raw = {"qdot": q8.q8_qdot_raw, "qmma": q8.q8_qmma_raw, "q50": q8.q8_q50_qdot_raw}[ops.kind]
+    if ops.kind == "qdotws":
+        wsb = q8.workspace(w.M, w.N, w.K, torch.device("cuda:0"))
+        wsp, wsn = wsb.data_ptr(), wsb.numel()
+
+        def raw(A, AS, W, WS, C, M, N, K, s):
+            return q8.q8_qdot_ws_raw(A, AS, W, WS, C, M, N, K, wsp, wsn, s)
+    else:
+        raw = {"qdot": q8.q8_qdot_raw, "qmma": q8.q8_qmma_raw, "q50": q8.q8_q50_qdot_raw}[ops.kind]
     ptrs = [(a.data_ptr(), s.data_ptr(), b.data_ptr(), t.data_ptr(), c.data_ptr()) for a, s, b, t, c in cps]
-    for k in range(warmup):
-        st = raw(*ptrs[k % len(ptrs)], w.M, w.N, w.K, sptr)
-        if st:
-            raise RuntimeError("%s failed: %s" % (ops.kind, q8.q8_strerror(st)))
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for k in range(steps):
-        raw(*ptrs[k % len(ptrs)], w.M, w.N, w.K, sptr)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    R = len(ptrs)
+    settle_copies(torch, ops, warmup % R)
+    gc.collect()
+    gc.disable()
+    try:
+        for k in range(warmup):
+            st = raw(*ptrs[k % R], w.M, w.N, w.K, sptr)
+            if st:
+                raise RuntimeError("%s failed: %s" % (ops.kind, q8.q8_strerror(st)))
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        for k in range(warmup, warmup + steps):
+            raw(*ptrs[k % R], w.M, w.N, w.K, sptr)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        gc.enable()
     ms = start.elapsed_time(end)
     return ms / steps, wall
 
@@ -380,6 +422,10 @@ def main():
         ("q50", synth.WORKLOADS[1]), ("q50", synth.WORKLOADS[2]), ("q50", synth.WORKLOADS[3]),
         ("qdot", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
         ("q50", synth.Workload(1, "q8_batch_m4_n14336_k4096", 4, 14336, 4096, False)),
+        # the long-contraction weights against a 32-row batch: the one-tile
+        # GEMM, then the split form of the workspace entry
+        ("qdot", synth.Workload(2, "q8_qgemm_m32_n4096_k14336_outliers", 32, 4096, 14336, True)),
+        ("qdotws", synth.Workload(2, "q8_qgemm_m32_n4096_k14336_outliers", 32, 4096, 14336, True)),
     ]
     late_variants = [] if (args.no_variants or args.profile) else [("qmma", synth.WORKLOADS[4])]
     if variants or late_variants:
@@ -389,7 +435,8 @@ def main():
         for kind, vw in todo:
             ops = Operands(torch, q8, vw, rotate=not args.no_rotate, kind=kind)
             ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
-            rec = {"entry": {"qdot": "q8_qdot", "qmma": "q8_qmma", "q50": "q8_q50_qdot"}[kind],
+            rec = {"entry": {"qdot": "q8_qdot", "qmma": "q8_qmma", "q50": "q8_q50_qdot",
+                             "qdotws": "q8_qdot_ws"}[kind],
                    "workload": vw.name, "M": vw.M, "N": vw.N, "K": vw.K,
                    "us_per_launch": round(ms3 * 1e3, 3),
                    "weight_bytes": ops.weight_bytes,
