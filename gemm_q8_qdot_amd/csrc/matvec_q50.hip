@@ -77,7 +77,27 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     // past the array; pieces past the group are not needed).  The next
     // group's pieces are loaded into registers while this group, already
     // parked in LDS, is decoded and computed.
+    // Rows of up to 256 blocks: the group's weight scales come with its
+    // pieces, one group ahead too (loaded when the group is about to be
+    // computed, their latency was exposed once per group: N=14336, K=4096
+    // 9.9 -> 9.6 us, M=4 14.2 -> 13.3 us); longer rows load them with the
+    // group (K=14336: 12.0 against 12.4 us ahead, where the extra registers
+    // cost more).
+    constexpr bool kWsAhead = T <= 4;
     v4i piece[kPieceRounds];
+    float ws_next[R][T];
+    auto load_ws = [&](int g, float (&ws)[R][T]) {
+        const int j0 = g * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int j = j0 + r;
+                const int b = lane + kWave * t;
+                const int64_t widx = WST ? (int64_t)b * N + j : (int64_t)j * KB + b;
+                ws[r][t] = (j < N && b < KB) ? WS[widx] : 0.0f;
+            }
+    };
     auto load_group = [&](int g) {
         const int gbase = g * R * row_bytes;
 #pragma unroll
@@ -85,6 +105,7 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             const int pc = lane + kWave * s;
             piece[s] = buffer_load16_nt(rW5, pc < pieces ? gbase + 16 * pc : kNoRead, 0);  // read once: streaming
         }
+        if constexpr (!PARTIALS && kWsAhead) load_ws(g, ws_next);
     };
     // The first group's pieces are in flight while the activation row is
     // staged (its latency and theirs overlap).
@@ -136,15 +157,14 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         const int j0 = g * R;
         float ws[R][T];
         if constexpr (!PARTIALS) {
+            if constexpr (kWsAhead) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const int j = j0 + r;
-                    const int b = lane + kWave * t;
-                    const int64_t widx = WST ? (int64_t)b * N + j : (int64_t)j * KB + b;
-                    ws[r][t] = (j < N && b < KB) ? WS[widx] : 0.0f;
-                }
+                    for (int t = 0; t < T; ++t) ws[r][t] = ws_next[r][t];
+            } else {
+                load_ws(g, ws);
+            }
         }
         // The previous group's reads of this area are done (one wave, in order).
         asm volatile("" ::: "memory");
