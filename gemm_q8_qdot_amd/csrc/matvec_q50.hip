@@ -86,8 +86,33 @@ matvec_q50_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     constexpr bool kWsAhead = T <= 4;
     v4i piece[kPieceRounds];
     float ws_next[R][T];
+    // Transposed scales with R = 2 or 4 consecutive rows per group: a lane's
+    // R scales of one block are adjacent (WST[b][j0 .. j0 + R - 1]) and come
+    // as one 8- or 16-byte load when N is a multiple of R and WS is aligned
+    // to it (else one 4-byte load per row and block, 64 cache lines per
+    // instruction).
+    const bool ws_vec = WST && (R == 2 || R == 4) && N % R == 0 &&
+                        (reinterpret_cast<uintptr_t>(WS) & (4 * R - 1)) == 0;
     auto load_ws = [&](int g, float (&ws)[R][T]) {
         const int j0 = g * R;
+        if constexpr (WST && (R == 2 || R == 4)) {
+            if (ws_vec) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int b = lane + kWave * t;
+                    const bool ok = j0 < N && b < KB;
+                    const float* src = WS + (ok ? (int64_t)b * N + j0 : 0);
+                    if constexpr (R == 4) {
+                        const float4 v = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+                        ws[0][t] = v.x; ws[1][t] = v.y; ws[2][t] = v.z; ws[3][t] = v.w;
+                    } else {
+                        const float2 v = ok ? *reinterpret_cast<const float2*>(src) : make_float2(0.f, 0.f);
+                        ws[0][t] = v.x; ws[1][t] = v.y;
+                    }
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -261,8 +286,16 @@ hipError_t launch_q5_t(const int8_t* A, const float* AS, const uint8_t* W5, cons
     // (K=4096: 11.0 -> 10.6 us against two rows per group and eight waves;
     // K=6144: 15.4 -> 14.2 us); longer rows one per group, eight waves (at
     // K=8192 sixteen tie, at K=14336 they are 12 % slower).
-    constexpr int R = T == 1 ? 4 : 1;
-    constexpr int kWavesPerCU = (T == 2 || T == 3) ? 16 : 8;
+    // Rows per wave group: four for rows of 64 blocks or less; with
+    // transposed scales also four for up to 192 blocks and two for up to 256
+    // (so that a lane's scales of one block arrive as one vector load).
+    constexpr int R = T == 1 ? 4 : (WST ? (T <= 3 ? 4 : (T == 4 ? 2 : 1)) : 1);
+    // Waves per compute unit: sixteen for rows of 65..192 blocks (one row a
+    // group), eight otherwise; twelve for the transposed-scale groups of two
+    // or four longer rows (their registers allow three waves per SIMD;
+    // measured N=14336, K=4096: 13.3 us against 13.7 with eight or sixteen,
+    // 21.8 us with one row a group and per-row scale gathers).
+    constexpr int kWavesPerCU = (WST && R > 1 && T > 1) ? 12 : ((T == 2 || T == 3) ? 16 : 8);
     constexpr int kPieceRounds = (R * T * kWave * kQ5BlockBytes + kWave * 16 - 1) / (kWave * 16);
     const int groups = (N + R - 1) / R;
     if constexpr (!PARTIALS) {
