@@ -130,13 +130,46 @@ def settle_copies(torch, ops: Operands, first: int):
     del acc
 
 
+_SPIN_CYCLES_PER_US = None
+
+
+def hold_stream(torch, us: float):
+    """Occupy the current stream with a spin kernel of about `us` microseconds.
+
+    Enqueued right before the start event, it keeps the GPU busy while the
+    host enqueues the timed launches, so the start event fires with the
+    launches already queued: the events then bracket back-to-back kernels,
+    not the host's latency to its first launch (several microseconds per
+    ctypes call), which would otherwise be spread over the steps.  The spin
+    rate (clock cycles per microsecond) is measured once with HIP events.
+    """
+    global _SPIN_CYCLES_PER_US
+    stream = torch.cuda.current_stream()
+    if _SPIN_CYCLES_PER_US is None:
+        cyc = 2_000_000
+        torch.cuda._sleep(cyc // 10)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(cyc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_US = cyc / max(e0.elapsed_time(e1) * 1e3, 1.0)
+    torch.cuda._sleep(int(us * _SPIN_CYCLES_PER_US))
+
+
 def time_launches(torch, q8, ops: Operands, steps: int, warmup: int):
     """Warm up, then time exactly `steps` launches between two HIP events.
 
     Launch k (warmup and timed alike, k = 0, 1, ...) reads rotated copy
     k mod R, so a timed launch never re-reads a copy a warmup launch just
     read unless there are fewer copies than launches.  The host's garbage
-    collector is held off while launches are issued.
+    collector is held off while launches are issued.  After the warmup the
+    stream is drained (synchronize), then held by a spin kernel long enough
+    for the host to enqueue every timed launch (1.5x the per-launch enqueue
+    time the warmup showed, plus 100 us), so that the two events bracket K
+    back-to-back kernels.
     """
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
@@ -156,13 +189,16 @@ def time_launches(torch, q8, ops: Operands, steps: int, warmup: int):
     gc.collect()
     gc.disable()
     try:
+        tw = time.perf_counter()
         for k in range(warmup):
             st = raw(*ptrs[k % R], w.M, w.N, w.K, sptr)
             if st:
                 raise RuntimeError("%s failed: %s" % (ops.kind, q8.q8_strerror(st)))
+        enqueue_us = (time.perf_counter() - tw) * 1e6 / max(warmup, 1) if warmup else 50.0
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
+        hold_stream(torch, min(1.5 * enqueue_us * steps + 100.0, 50_000.0))
         t0 = time.perf_counter()
         start.record(stream)
         for k in range(warmup, warmup + steps):
@@ -195,13 +231,16 @@ def time_quantize(torch, q8, rows: int, K: int, steps: int, warmup: int, rotate:
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     ptrs = [(x.data_ptr(), q.data_ptr(), d.data_ptr()) for x, q, d in bufs]
+    tw = time.perf_counter()
     for k in range(warmup):
         st = q8.q8_quantize_raw(*ptrs[k % R], rows, K, sptr)
         if st:
             raise RuntimeError("q8_quantize failed: %s" % q8.q8_strerror(st))
+    enqueue_us = (time.perf_counter() - tw) * 1e6 / max(warmup, 1) if warmup else 50.0
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    hold_stream(torch, min(1.5 * enqueue_us * steps + 100.0, 50_000.0))
     start.record(stream)
     for k in range(steps):
         q8.q8_quantize_raw(*ptrs[k % R], rows, K, sptr)
