@@ -1,11 +1,10 @@
 // Q8_0 matvec for small M (decode step): C[i, :] = qdot_t(A[i, :], AS[i, :], W, WS).
 //
 // What is computed: the qdot_t row of the Q8_0 table ("Phobos Language Spec",
-// section "Quantized built-ins"), with the inner block sum in integers as the
-// "Quantized built-ins and formats" page's Q8_0 section describes, and the
-// weights read at their stored size (that page's introduction: raw block bytes
-// are decoded in registers, so weights cross the memory bus at 1 byte per
-// value plus the block scale).
+// section "Quantized built-ins"); each block sum is an integer dot product
+// ("Quantized built-ins and formats", section "Q8_0").  The weights come from
+// HBM exactly as stored, one byte per value and one f32 scale per 32 values,
+// and only the kernel turns them into products (same page, introduction).
 //
 // Prior art on the pages: the q8_qdot decode kernel (one activation row
 // against 64 output columns per CTA, Q8_0 section) and lanes_matvec (one warp

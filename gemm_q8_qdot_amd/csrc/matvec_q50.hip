@@ -6,9 +6,9 @@
 // as Q5_0 blocks without their scale -- per 32 values 20 bytes, the qh word
 // then 16 bytes whose byte e holds element e (low nibble) and element e + 16
 // (high nibble); element value q - 16, q the 5-bit number with bit e of qh
-// (little-endian) as bit 4.  Weights cross the bus at 20 bytes per 32 values
-// plus the 4-byte scale ("Quantized built-ins and formats", introduction:
-// decoded in registers).
+// (little-endian) as bit 4.  The 20 bytes per 32 values plus the 4-byte
+// scale are all that is read of the weights; the codes are rebuilt in
+// registers ("Quantized built-ins and formats", introduction).
 //
 // Design for CDNA4 wave64: lane l owns whole blocks b = l + 64 t of a row;
 // the rows arrive as contiguous 1 KiB wave loads staged in LDS (see the
