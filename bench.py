@@ -144,6 +144,9 @@ def hold_stream(torch, us: float):
     rate (clock cycles per microsecond) is measured once with HIP events.
     """
     global _SPIN_CYCLES_PER_US
+    if not hasattr(torch.cuda, "_sleep"):
+        log("[bench] torch.cuda._sleep is missing: timed windows start without a held stream")
+        return
     stream = torch.cuda.current_stream()
     if _SPIN_CYCLES_PER_US is None:
         cyc = 2_000_000
