@@ -453,10 +453,21 @@ matvec_rows_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     } else {
         v4i w[S];
         float ws[S];
-        if (wave < N) load_row(wave, w, ws);
+        // A wave's rows: every nwaves-th; but for one activation row where
+        // each wave has one or two rows (nwaves < N <= 2 nwaves), the two
+        // neighbouring rows 2w and 2w + 1, which streams better (measured:
+        // N=4096, K=4096 5.0-5.1 -> 4.73 us, K=6144 6.44 -> 6.21 us; N=3000,
+        // K=4096 4.37 -> 4.30 us).  Runs of neighbouring rows were slower
+        // with more rows per wave (N=14336, K=4096, eight a wave: 11.4 ->
+        // 11.9 us) and in the batch form (M=4, N=14336: 14.2 -> 15.9 us).
+        const bool pairs = !MULTI && N > nwaves && N <= 2 * nwaves;
+        const int j0 = pairs ? 2 * wave : wave;
+        const int jend = pairs ? (2 * wave + 2 < N ? 2 * wave + 2 : N) : N;
+        const int step = pairs ? 1 : nwaves;
+        if (j0 < jend) load_row(j0, w, ws);
         stage_batch();
-        for (int j = wave; j < N; j += nwaves) {
-            if (j != wave) load_row(j, w, ws);
+        for (int j = j0; j < jend; j += step) {
+            if (j != j0) load_row(j, w, ws);
             compute_row(j, w, ws);
         }
     }
