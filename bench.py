@@ -435,6 +435,19 @@ def main():
         % (ms * 1e3, weight_gbs, achieved, 100 * achieved / HBM_PEAK_GBS))
     del head
     torch.cuda.empty_cache()
+    if not args.profile and not args.no_rotate:
+        # The same launches on one copy read over and over: after the first
+        # launch the operands come from the 256 MB last-level cache.  A
+        # cache-warm figure, for context only (never the headline).
+        warm = Operands(torch, q8, head_w, rotate=False)
+        msw, _ = time_launches(torch, q8, warm, args.steps, args.warmup)
+        result["cache_warm"] = {"us_per_launch": round(msw * 1e3, 3),
+                                "gbs": round(warm.algo_bytes / (msw * 1e-3) / 1e9, 1),
+                                "note": "one operand copy re-read by every launch (served from the "
+                                        "last-level cache); context only"}
+        log("[bench] headline cache-warm: %.3f us/launch" % (msw * 1e3))
+        del warm
+        torch.cuda.empty_cache()
 
     # The small workloads, before the GEMMs.
     others = [int(x) for x in args.others.split(",") if x.strip() != ""]
