@@ -154,9 +154,10 @@ int q8_qdot_partials(const int8_t *A, const int8_t *W, int32_t *P,
 /*
  * The same contractions with a caller workspace (qdot_t / qmma_t as for
  * q8_qdot_stream and q8_qmma; "Phobos Language Spec", section "Quantized
- * built-ins", Q8_0 table).  For M >= 8 shapes whose 64 x 64 output tiles are
- * too few to occupy the GPU (for example M = 64, N = 4096), the contraction
- * is split into slices of K/32 blocks across workgroups; each writes its
+ * built-ins", Q8_0 table).  For M >= 8 shapes with K >= 8192 whose 64 x 64
+ * output tiles are too few to occupy the GPU (for example M = 32, N = 4096,
+ * K = 14336), the contraction is split into slices of K/32 blocks across
+ * workgroups; each writes its
  * partial f32 tile to the workspace and the last of a tile's workgroups to
  * finish adds the partial tiles in slice order (so the result does not
  * depend on the order in which they finish) and stores C.
