@@ -58,6 +58,7 @@ def _t(x, dev):
 # (entry, M, N, K): the kernel each shape reaches is in the comment.
 CASES = [
     ("qdot", 1, 5000, 4096),      # one-row decode kernel, rows per wave ragged
+    ("qdot", 1, 3001, 4096),      # one-row decode kernel, neighbouring-row pairs, odd N
     ("qdot", 1, 3000, 9248),      # one-row decode kernel, prefetching form
     ("qdot", 1, 130, 16416),      # chunked matvec (rows longer than 16 KiB)
     ("qdot", 3, 1000, 4128),      # small-batch matvec
@@ -134,3 +135,57 @@ def test_quantize_bounds(dev, rows, K):
     Qref, Dref = oracle.quantize_rows(X)
     assert np.array_equal(Q.cpu().numpy(), Qref)
     assert np.array_equal(D.cpu().numpy().view(np.uint32), Dref.view(np.uint32))
+
+
+# The workspace entries' split form (K >= 8192, few 64 x 64 tiles), with
+# ragged M and N and a partial last slice; the workspace itself sits in a
+# guarded buffer too: nothing past the size q8_qdot_ws_size reports may be
+# written, and its tile counters must be back at zero.
+WS_CASES = [
+    ("qdot_ws", 40, 1000, 8320),
+    ("qmma_ws", 70, 300, 8224),
+    ("noalloc", 33, 700, 9216),
+]
+
+
+@pytest.mark.parametrize("entry,M,N,K", WS_CASES)
+def test_split_output_and_workspace_bounds(dev, entry, M, N, K):
+    _say("[guard] %s M=%d N=%d K=%d" % (entry, M, N, K))
+    KB = K // 32
+    need = q8.q8_qdot_ws_size(M, N, K)
+    assert need > 0, "shape expected to take the split form"
+    seed = M * 131 + N * 7 + K
+    A = synth.random_i8((M, K), seed)
+    AS = synth.random_scales((M, KB), seed + 1, 1e-3, 1.0)
+    WS = synth.random_scales((N, KB), seed + 2, 1e-3, 1.0)
+    W = synth.random_i8((N, K), seed + 3)
+    ws_t = entry == "qmma_ws"
+    WSx = np.ascontiguousarray(WS.T) if ws_t else WS
+    tA, tAS, tW, tWS = _t(A, dev), _t(AS, dev), _t(W, dev), _t(WSx, dev)
+
+    cbuf, C = _guarded(M * N, torch.float32, dev)
+    C = C.view(M, N)
+    # workspace: zero-filled need bytes, then sentinel words
+    wbuf = torch.full(((need + 3) // 4 + GUARD,), SENTINEL, dtype=torch.int32, device=dev)
+    wbuf[:(need + 3) // 4] = 0
+    ws = wbuf.view(torch.uint8)[:need]
+    if entry == "qdot_ws":
+        q8.q8_qdot_ws(tA, tAS, tW, tWS, ws, C)
+    elif entry == "qmma_ws":
+        q8.q8_qmma_ws(tA, tAS, tW, tWS, ws, C)
+    else:
+        st = q8.q8_qdot_noalloc_raw(tA.data_ptr(), tAS.data_ptr(), tW.data_ptr(), tWS.data_ptr(),
+                                    C.data_ptr(), M, N, K, torch.cuda.current_stream().cuda_stream)
+        assert st == q8.Q8_OK, q8.q8_strerror(st)
+    pbuf, P = _guarded(M * N * KB, torch.int32, dev)
+    P = P.view(M, N, KB)
+    q8.q8_qdot_ws_partials(tA, tW, P)
+    torch.cuda.synchronize()
+    _check_guard(cbuf, M * N, entry + " C")
+    _check_guard(pbuf, M * N * KB, entry + " P")
+    host = wbuf.cpu().numpy()
+    assert (host[(need + 3) // 4:] == SENTINEL).all(), "%s: wrote past the workspace" % entry
+    assert (host[:1024] == 0).all(), "%s: tile counters not reset" % entry
+    assert np.array_equal(P.cpu().numpy(), oracle.block_partials(A, W))
+    out, mag = (oracle.qmma_f64 if ws_t else oracle.qdot_f64)(A, AS, W, WSx)
+    assert oracle.within_tolerance(C.cpu().numpy(), out, mag).all()
