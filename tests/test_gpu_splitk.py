@@ -202,3 +202,31 @@ def test_split_graph_replay(dev):
         assert np.array_equal(C.cpu().numpy().view(np.uint32), eager.view(np.uint32)), "replay %d" % r
         assert np.array_equal(other.cpu().numpy().view(np.uint32), eager.view(np.uint32))
     assert _counters_zero(ws, M, N)
+
+
+def test_two_streams_two_workspaces(dev):
+    # calls on two streams, each with its own workspace, interleaved: every
+    # result is the eager single-stream one, bit for bit
+    shapes = [(32, 4096, 8192), (40, 1000, 8320)]
+    cases = []
+    for k, (M, N, K) in enumerate(shapes):
+        host = _case(M, N, K, 1700 + k)
+        t = tuple(_dev(x, dev) for x in host)
+        ref = q8.q8_qdot_ws(*t, q8.workspace(M, N, K, dev))
+        cases.append((t, ref, q8.workspace(M, N, K, dev), (M, N, K)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = [[], []]
+    for rep in range(3):
+        for k, (t, ref, ws, (M, N, K)) in enumerate(cases):
+            with torch.cuda.stream(streams[k]):
+                C = torch.empty((M, N), dtype=torch.float32, device=dev)
+                q8.q8_qdot_ws(*t, ws, C, stream=streams[k])
+                outs[k].append(C)
+    torch.cuda.synchronize()
+    for k, (t, ref, ws, shape) in enumerate(cases):
+        for C in outs[k]:
+            assert torch.equal(C.view(torch.int32), ref.view(torch.int32)), "stream %d %s" % (k, shape)
+        assert _counters_zero(ws, *shape[:2])
