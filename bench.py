@@ -37,8 +37,11 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POP/s)
-# VALU lane-op rate with packed-FP32 forms off: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz.
-VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
+# VALU f32 FMA lane-op rate: 256 CU x 4 SIMD x 32 lanes x 2.4 GHz, the published
+# 157.3 TFLOP/s FP32 vector figure.  Plain v_fma_f32 (packed forms are not used)
+# reaches it on this part: measured, a SIMD with two or more waves issuing
+# independent wave64 FMAs completes one every 2.0-2.4 clocks.
+VALU_LANE_OPS_PER_S = 256 * 4 * 32 * 2.4e9
 EPILOGUE_VALU_OPS = 2            # f32 VALU ops per (i, j, block) in the MFMA epilogue
 CACHE_DEFEAT_BYTES = 1 << 30     # rotate >= 1 GiB of distinct operand copies
 KERNEL_NAMES = ("matvec", "qgemm_ksplit", "qgemm_staged")          # by q8_qdot_path
