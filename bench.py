@@ -472,6 +472,34 @@ def main():
         del ops
         torch.cuda.empty_cache()
 
+    # One GPU's share of an 8-way split: the kernel at the shape each GPU
+    # would run (N split: a slab of weight rows; K split: 1/8 of the blocks,
+    # whose f32 partial outputs an all-reduce would sum).  No collective is
+    # timed; same generators, seeds of the full workload, fewer rows or k.
+    shares = [] if (args.no_variants or args.profile) else [
+        ("N/8", synth.WORKLOADS[1], synth.Workload(1, "q8_matvec_m1_n1792_k4096", 1, 1792, 4096, False)),
+        ("K/8", synth.WORKLOADS[2], synth.Workload(2, "q8_matvec_m1_n4096_k1792_outliers", 1, 4096, 1792, True)),
+        ("N/8", synth.WORKLOADS[3], synth.Workload(3, "q8_qgemm_m64_n512_k4096", 64, 512, 4096, False)),
+        ("N/8", synth.WORKLOADS[4], synth.Workload(4, "q8_qgemm_m512_n1792_k4096", 512, 1792, 4096, False)),
+    ]
+    if shares:
+        result["shard_share"] = []
+    for split, full, sw_ in shares:
+        ops = Operands(torch, q8, sw_, rotate=not args.no_rotate)
+        ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
+        rec = {"split": split, "of": full.name, "workload": sw_.name, "M": sw_.M, "N": sw_.N, "K": sw_.K,
+               "kernel": KERNEL_NAMES[q8.q8_qdot_path(sw_.M, sw_.N, sw_.K)],
+               "us_per_launch": round(ms3 * 1e3, 3),
+               "hbm_gbs": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9, 1),
+               "hbm_frac": round(ops.algo_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "int8_tops": round(ops.int8_ops / (ms3 * 1e-3) / 1e12, 2)}
+        result["shard_share"].append(rec)
+        log("[bench] %s share of %s (%s): %.3f us/launch, %.1f GB/s (%.1f%% HBM), %.1f int8 TOPS"
+            % (split, full.name, sw_.name, rec["us_per_launch"], rec["hbm_gbs"], 100 * rec["hbm_frac"],
+               rec["int8_tops"]))
+        del ops
+        torch.cuda.empty_cache()
+
     # The other entry points and dispatch paths, on the same workload shapes:
     # qmma_t (transposed scales), Q5_0 weights, and a small decode batch.
     # The qmma_t GEMM is timed with the other GEMM, last.
