@@ -44,8 +44,8 @@ INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published (5.0 POP/s)
 VALU_LANE_OPS_PER_S = 256 * 4 * 32 * 2.4e9
 EPILOGUE_VALU_OPS = 2            # f32 VALU ops per (i, j, block) in the MFMA epilogue
 CACHE_DEFEAT_BYTES = 1 << 30     # rotate >= 1 GiB of distinct operand copies
-KERNEL_NAMES = ("matvec", "qgemm_ksplit", "qgemm_staged")          # by q8_qdot_path
-KERNEL_SOURCES = ("matvec.hip", "qgemm_ksplit.hip", "qgemm.hip")   # their csrc files
+KERNEL_NAMES = ("matvec", "qgemm_ksplit", "qgemm_staged", "qgemm_splitk")              # by q8_qdot_path
+KERNEL_SOURCES = ("matvec.hip", "qgemm_ksplit.hip", "qgemm.hip", "qgemm_splitk.hip")   # their csrc files
 
 
 def log(msg):

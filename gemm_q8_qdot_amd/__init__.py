@@ -385,7 +385,8 @@ def q8_quantize(X, Q=None, D=None, stream=None):
 
 
 def q8_qdot_path(M: int, N: int, K: int) -> int:
-    """0 = wave64 matvec, 1 = MFMA GEMM (K split across a workgroup), 2 = MFMA GEMM (LDS-staged tiles)."""
+    """0 = wave64 matvec, 1 = MFMA GEMM (K split across a workgroup), 2 = MFMA GEMM (LDS-staged
+    128 x 224 tiles), 3 = MFMA GEMM (64 x 64 tiles over all of K through an LDS ring)."""
     st = load().q8_qdot_path(M, N, K)
     if st < 0:
         raise Q8Error(st, "q8_qdot_path")

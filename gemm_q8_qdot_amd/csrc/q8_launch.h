@@ -70,6 +70,11 @@ bool splitk_plan(int M, int N, int K, int* S, int* slice_blocks, size_t* ws_byte
 hipError_t launch_qgemm_splitk(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                                float* C, int32_t* P, int M, int N, int K, bool ws_t, int S,
                                int slice_blocks, void* workspace, hipStream_t stream);
+// The same kernel over all of K (S = 1, slice_blocks = splitk_whole_k_blocks,
+// no workspace): taken instead of the K-split GEMM where its 64 x 64 tiles
+// need fewer rounds of workgroups (splitk_whole_k).
+bool splitk_whole_k(int M, int N, int K);
+int splitk_whole_k_blocks(int K);
 // The same with the library's file-scope scratch array as the workspace (no
 // allocation); splitk_scratch_capacity() is the largest workspace it stands
 // for.  Calls that overlap on one GPU race on it.

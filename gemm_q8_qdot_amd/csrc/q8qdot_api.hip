@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: workspace and no-allocation entries
+constexpr int kVersion = 201;  // 0.2.1: medium GEMMs on 64 x 64 tiles over all of K (path 3)
 constexpr int kMatvecMaxM = 7;  // M < 8 -> matvec; the MFMA path needs 8+ rows to pay off
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -31,6 +31,14 @@ int check_range(int64_t M, int64_t N, int64_t K, bool partials) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ELAUNCH; }
+
+// The block GEMM a Q8_0 shape with M >= 8 takes (q8_qdot_path's numbers):
+// 1 = K-split (32 x 32 tiles), 2 = LDS-staged (128 x 224 tiles), 3 = the
+// 64 x 64-tile ring kernel over all of K (the split-K kernel's one-slice form).
+int gemm_path(int M, int N, int K) {
+    const int v = q8::qgemm_variant(M, N, K);
+    return v == 1 && q8::splitk_whole_k(M, N, K) ? 3 : v;
+}
 
 // ws_t: WS is the qmma_t form, stored transposed [K/32][N].  split: the
 // workspace entries -- shapes with few output tiles take the split-K GEMM
@@ -72,6 +80,9 @@ int run_qdot(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
             return status_of(q8::launch_qgemm_splitk(A, AS, W, WS, C, P, M, N, K, ws_t, S, sb,
                                                      workspace, stream));
     }
+    if (M > kMatvecMaxM && gemm_path(M, N, K) == 3)
+        return status_of(q8::launch_qgemm_splitk(A, AS, W, WS, C, P, M, N, K, ws_t, 1,
+                                                 q8::splitk_whole_k_blocks(K), nullptr, stream));
     hipError_t e = M <= kMatvecMaxM
                        ? q8::launch_matvec(A, AS, W, WS, C, P, M, N, K, ws_t, stream)
                        : q8::launch_qgemm(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
@@ -227,7 +238,7 @@ Q8_API int q8_q50_partials(const int8_t* A, const uint8_t* W5, int32_t* P, int M
 Q8_API int q8_qdot_path(int M, int N, int K) {
     int st = check_shape(M, N, K);
     if (st != Q8_OK) return st;
-    return M <= kMatvecMaxM ? 0 : q8::qgemm_variant(M, N, K);
+    return M <= kMatvecMaxM ? 0 : gemm_path(M, N, K);
 }
 
 Q8_API int q8_quantize(const float* X, int8_t* Q, float* D, int rows, int K, void* stream) {

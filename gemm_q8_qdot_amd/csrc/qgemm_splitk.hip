@@ -376,6 +376,29 @@ bool splitk_plan(int M, int N, int K, int* S_out, int* slice_blocks_out, size_t*
     return true;
 }
 
+// The kernel over all of K (one slice: no workspace, C stored directly)
+// against the K-split GEMM (one 32 x 32 tile per workgroup), for the shapes
+// that kernel would take.  Both place one workgroup per compute unit (their
+// LDS), so their time goes with their rounds of workgroups: a 64 x 64 tile
+// over all of K costs about 2.45 times a 32 x 32 one (it brings in twice the
+// rows and computes four times the outputs, sharing each row four ways).
+// Measured on MI355X (us, K-split against this kernel, K = 4096): 512 x
+// 1792 (4 rounds against 1) 32.2 / 21.5; 256 x 4096 (4 / 1) 34.7 / 22.5;
+// 300 x 2000 (3 / 1) 25.3 / 20.9; 128 x 4096 (2 / 1) 18.2 / 20.6; 96 x 4096
+// (2 / 1) 17.6 / 20.2; 512 x 1024 (2 / 1) 17.2 / 20.3.
+bool splitk_whole_k(int M, int N, int K) {
+    if (M < 8 || N < 1 || K < kBlock || (int64_t)K * kSkM > INT32_MAX) return false;
+    const int64_t cus = device_cu_count();
+    const int64_t t32 = ((int64_t)M + kTile - 1) / kTile * (((int64_t)N + kTile - 1) / kTile);
+    const int64_t t64 = ((int64_t)M + kSkM - 1) / kSkM * (((int64_t)N + kSkN - 1) / kSkN);
+    if (t64 > 0x7FFFFFFF) return false;
+    const int64_t r32 = (t32 + cus - 1) / cus;
+    const int64_t r64 = (t64 + cus - 1) / cus;
+    return 100 * r32 > 245 * r64;
+}
+
+int splitk_whole_k_blocks(int K) { return (K / kBlock + kSkSB - 1) / kSkSB * kSkSB; }
+
 namespace {
 
 hipError_t launch_splitk(const int8_t* A, const float* AS, const int8_t* W, const float* WS,

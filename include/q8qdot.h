@@ -213,7 +213,12 @@ int q8_qdot_noalloc(const int8_t *A, const float *AS, const int8_t *W, const flo
  * int8-MFMA block GEMM, 1 = one workgroup per
  * 32 x 32 output tile with the K/32 blocks split across its waves (few
  * tiles: small M or N), 2 = LDS-staged 128 x 224 workgroup tiles (large M
- * and N).  Q8_EINVAL for bad shapes.
+ * and N), 3 = one workgroup per 64 x 64 output tile over all of K, staged
+ * through an LDS ring (medium shapes: too few 128 x 224 tiles to fill the
+ * chip, but so many 32 x 32 tiles that one workgroup per 64 x 64 tile needs
+ * far fewer rounds of workgroups; the kernel of q8_qdot_ws's split form,
+ * with one slice and no workspace).  The debug entry q8_qdot_partials takes
+ * the same kernel.  Q5_0 weights take 0 or 1.  Q8_EINVAL for bad shapes.
  */
 int q8_qdot_path(int M, int N, int K);
 

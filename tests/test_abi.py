@@ -69,6 +69,12 @@ def test_path_dispatch(lib):
     assert q8.q8_qdot_path(512, 14336, 4096) == 2
     assert q8.q8_qdot_path(129, 14336, 96) == 2
     assert q8.q8_qdot_path(128, 449, 512) == 1
+    # many 32 x 32 tiles but too few 128 x 224 ones: 64 x 64 tiles over all of K
+    # (on a 256-compute-unit part: 896 against 224 tiles, 4 rounds against 1)
+    assert q8.q8_qdot_path(512, 1792, 4096) == 3
+    assert q8.q8_qdot_path(256, 4096, 1024) == 3
+    assert q8.q8_qdot_path(128, 4096, 4096) == 1     # 512 against 128 tiles: 2 rounds against 1
+    assert q8.q8_qdot_path(16, 40000, 4096) == 1     # 64-row tiles would be three quarters empty
     assert lib.q8_qdot_path(1, 1, 33) == q8.Q8_EINVAL
     assert lib.q8_qdot_path(-1, 1, 32) == q8.Q8_EINVAL
 

@@ -4,7 +4,7 @@ The plain entries keep no state between calls (no device buffers of their
 own; only per-device launch settings, set once), so calls that overlap on
 different streams, issued from one host thread or from several, must give
 exactly what the same calls give one after another.  Every kernel family is
-covered (the one-row and small-batch decode kernels, both GEMMs, transposed
+covered (the one-row and small-batch decode kernels, the three GEMMs, transposed
 weight scales, Q5_0 weights, the debug partials and the quantizer).  The
 reference is the library's own serial result on the same inputs, so the
 comparison is bitwise; the oracle parity of each kernel is covered by the
@@ -32,6 +32,7 @@ CASES = [
     ("qdot", 4, 2048, 4096, 0),
     ("qdot", 64, 1024, 4096, 1),
     ("qdot", 256, 14336, 1024, 2),
+    ("qdot", 300, 2000, 1056, 3),
     ("qmma", 64, 1024, 4096, 1),
     ("q50", 1, 4096, 4096, None),
     ("partials", 16, 512, 4096, 1),

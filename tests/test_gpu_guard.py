@@ -64,13 +64,20 @@ CASES = [
     ("qdot", 3, 1000, 4128),      # small-batch matvec
     ("qdot", 70, 300, 1056),      # K-split MFMA GEMM
     ("qdot", 129, 14336, 96),     # LDS-staged MFMA GEMM, ragged M
+    ("qdot", 300, 2000, 1056),    # 64 x 64-tile GEMM over all of K, ragged M, N, K
     ("qmma", 1, 1000, 4096),      # matvec with transposed scales
     ("qmma", 5, 1000, 2080),      # small batch with transposed scales
     ("qmma", 130, 14300, 128),    # staged GEMM with transposed scales
+    ("qmma", 270, 1900, 544),     # 64 x 64-tile GEMM with transposed scales
     ("q50", 1, 1001, 4096),       # Q5_0 matvec
     ("q50", 9, 100, 1056),        # Q5_0 K-split GEMM
     ("q50t", 2, 333, 2048),       # Q5_0 matvec, transposed scales
 ]
+
+
+def test_cases_reach_every_q8_path():
+    paths = {q8.q8_qdot_path(M, N, K) for entry, M, N, K in CASES if entry in ("qdot", "qmma")}
+    assert paths == {0, 1, 2, 3}
 
 
 @pytest.mark.parametrize("entry,M,N,K", CASES)

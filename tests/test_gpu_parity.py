@@ -182,8 +182,10 @@ def test_small_batch(dev, M, N, K):
     _check_full(A, AS, W, WS, dev, "batch")
 
 
-# one row, a small batch, the K-split GEMM, the LDS-staged GEMM
-@pytest.mark.parametrize("M,N,K", [(1, 3000, 4096), (4, 3000, 4096), (64, 512, 2048), (256, 14336, 256)])
+# one row, a small batch, the K-split GEMM, the LDS-staged GEMM, the
+# 64 x 64-tile GEMM over all of K
+@pytest.mark.parametrize("M,N,K", [(1, 3000, 4096), (4, 3000, 4096), (64, 512, 2048), (256, 14336, 256),
+                                   (300, 2000, 1024)])
 def test_cancelling_half_blocks(dev, M, N, K):
     A, AS, W, WS = synth.cancelling_blocks(M, N, K, 880 + M)
     P = oracle.block_partials(A, W)
@@ -230,9 +232,38 @@ def test_staged_gemm_shapes(dev, M, N, K):
     _check_partials_sliced(P, A, W, "staged P")
 
 
+# The 64 x 64-tile GEMM over all of K: the M=512 workload's 8-way N share at
+# its full K, and ragged M, N and K (a partial last stage of blocks).
+WHOLE_K = [(512, 1792, 4096), (300, 2000, 1056), (270, 1900, 544)]
+
+
+@pytest.mark.parametrize("M,N,K", WHOLE_K)
+def test_whole_k_gemm_shapes(dev, M, N, K):
+    assert q8.q8_qdot_path(M, N, K) == 3
+    seed = M * 11 + N * 5 + K
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 10.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-4, 1.0)
+    _say("[parity] whole-K GEMM M=%d N=%d K=%d" % (M, N, K))
+    tA, tAS, tW, tWS = (_dev(x, dev) for x in (A, AS, W, WS))
+    C = q8.q8_qdot(tA, tAS, tW, tWS)
+    P = q8.q8_qdot_partials(tA, tW)
+    WST = np.ascontiguousarray(WS.T)
+    C2 = q8.q8_qmma(tA, tAS, tW, _dev(WST, dev))
+    torch.cuda.synchronize()
+    out, mag = oracle.qdot_f64(A, AS, W, WS)
+    _assert_close(C.cpu().numpy(), out, mag, "whole-K C")
+    out, mag = oracle.qmma_f64(A, AS, W, WST)
+    _assert_close(C2.cpu().numpy(), out, mag, "whole-K C (qmma)")
+    _check_partials_sliced(P, A, W, "whole-K P")
+
+
 # one row, the K-split GEMM (M = 9, and M = 129 with few tiles), the
-# LDS-staged GEMM (M = 129 with N = 14336)
-@pytest.mark.parametrize("M,N,K", [(1, 70, 1024), (9, 70, 1024), (129, 70, 1024), (129, 14336, 256)])
+# LDS-staged GEMM (M = 129 with N = 14336), the 64 x 64-tile GEMM over all
+# of K (M = 300, N = 2000)
+@pytest.mark.parametrize("M,N,K", [(1, 70, 1024), (9, 70, 1024), (129, 70, 1024), (129, 14336, 256),
+                                   (300, 2000, 1024)])
 def test_extreme_bytes_and_scales(dev, M, N, K):
     A = np.full((M, K), -128, np.int8)
     W = synth.random_i8((N, K), 77)
@@ -254,7 +285,7 @@ def test_extreme_bytes_and_scales(dev, M, N, K):
         WS[3:40, b] = np.float32(2.0 ** e)
         AS[:, b] = np.float32(2.0 ** -e)
     if M > 1:
-        assert q8.q8_qdot_path(M, N, K) == (2 if N == 14336 else 1)
+        assert q8.q8_qdot_path(M, N, K) == (2 if N == 14336 else 3 if N == 2000 else 1)
     _check_full(A, AS, W, WS, dev, "extreme")
     WST = np.ascontiguousarray(WS.T)
     C2 = q8.q8_qmma(_dev(A, dev), _dev(AS, dev), _dev(W, dev), _dev(WST, dev))

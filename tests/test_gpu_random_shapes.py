@@ -2,8 +2,9 @@
 
 The shapes are drawn once from a fixed seed so that each dispatch regime is
 reached several times with sizes nobody picked by hand: one activation row,
-small batches (2..7 rows), the K-split GEMM (few output tiles) and the
-LDS-staged GEMM (M >= 128 and many tiles, short K); N and K/32 are
+small batches (2..7 rows), the K-split GEMM (few output tiles), the
+LDS-staged GEMM (M >= 128 and many tiles, short K) and the 64 x 64-tile GEMM
+over all of K (medium M x N, short K); N and K/32 are
 ragged (any value; one activation row up to 600 blocks, past the 16 KiB
 rows of the one-row kernels).  Each case runs q8_qdot, q8_qmma (the same
 scales transposed), q8_q50_qdot and q8_q50_qmma (Q5_0 weights) and both
@@ -44,6 +45,14 @@ def _draw_cases(per_regime=6, seed=20261202):
         M = int(rng.integers(128, 601))
         n_min = 224 * (-(-128 // -(-M // 128)))
         cases.append((M, int(rng.integers(n_min, n_min + 3000)), 32 * int(rng.integers(1, 9))))
+    for _ in range(per_regime):       # 520..1000 tiles of 32 x 32 (three or four
+        # rounds on 256 compute units), one round of 64 x 64 tiles, too few
+        # 128 x 224 tiles: the 64 x 64-tile GEMM over all of K, short K
+        M = int(rng.integers(64, 601))
+        mt = -(-M // 32)
+        nt = int(rng.integers(-(-520 // mt), 1000 // mt + 1))
+        N = 32 * nt - int(rng.integers(0, 32))
+        cases.append((M, N, 32 * int(rng.integers(1, 9))))
     return cases
 
 
@@ -116,9 +125,10 @@ def test_random_shape_all_entries(dev, case):
 
 def test_cases_reach_every_path():
     # each regime of the draw lands on its dispatch path (0 matvec,
-    # 1 K-split GEMM, 2 LDS-staged GEMM)
+    # 1 K-split GEMM, 2 LDS-staged GEMM, 3 64 x 64-tile GEMM over all of K)
     paths = [q8.q8_qdot_path(M, N, K) for M, N, K in CASES]
-    per = len(CASES) // 4
+    per = len(CASES) // 5
     assert paths[:2 * per] == [0] * (2 * per)
     assert paths[2 * per:3 * per] == [1] * per
-    assert paths[3 * per:] == [2] * per
+    assert paths[3 * per:4 * per] == [2] * per
+    assert paths[4 * per:] == [3] * per, CASES[4 * per:]
