@@ -170,3 +170,51 @@ def test_range_overflow_rejected(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         q8.load(str(tmp_path / "missing.so"))
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "q8qdot.h"
+
+int main(void) {
+    int8_t dummy[32];
+    printf("version %d\n", q8_version());
+    printf("path %d %d %d %d\n", q8_qdot_path(1, 4096, 4096), q8_qdot_path(64, 4096, 4096),
+           q8_qdot_path(512, 14336, 4096), q8_qdot_path(1, 1, 33));
+    printf("einval %d\n", q8_qdot(dummy, 0, dummy, 0, 0, 1, 1, 33));
+    printf("enull %d\n", q8_qdot_stream(0, 0, 0, 0, 0, 1, 1, 32, 0));
+    printf("ealign %d\n", q8_qdot_partials(dummy + 1, dummy, (int32_t *)0 + 1, 1, 1, 32, 0));
+    printf("empty %d\n", q8_quantize(0, 0, 0, 0, 32, 0));
+    printf("strerror %s\n", q8_strerror(Q8_ELAUNCH));
+    return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(tmp_path, lib):
+    # The header is plain C (C99, no C++): a C program includes it, links
+    # the library and reaches the host-side validation of several entries.
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(q8.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I" + os.path.join(ROOT, "include"),
+           str(src), "-o", str(exe), "-L" + libdir, "-l:" + os.path.basename(q8.LIB_PATH),
+           "-Wl,-rpath," + libdir]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    out = dict(line.split(" ", 1) for line in r.stdout.strip().split("\n"))
+    assert int(out["version"]) == q8.q8_version()
+    assert out["path"].split() == ["0", "1", "2", str(q8.Q8_EINVAL)]
+    assert int(out["einval"]) == q8.Q8_EINVAL
+    assert int(out["enull"]) == q8.Q8_ENULL
+    assert int(out["ealign"]) == q8.Q8_EALIGN
+    assert int(out["empty"]) == q8.Q8_OK
+    assert out["strerror"] == q8.q8_strerror(q8.Q8_ELAUNCH)
