@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--no-rotate", action="store_true", help="reuse one copy (cache-warm number)")
     ap.add_argument("--profile", action="store_true",
                     help="only launch the headline kernel (for rocprofv3 counter passes)")
+    ap.add_argument("--shape", default="", metavar="M,N,K",
+                    help="with --profile: launch this shape instead (generators and seeds of --workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB 10 times and exit (counter calibration)")
     return ap.parse_args()
@@ -402,6 +404,11 @@ def main():
         args.warmup = min(args.warmup, 5)
 
     head_w = synth.WORKLOADS[args.workload]
+    if args.shape:
+        if not args.profile:
+            sys.exit("bench.py: --shape is for --profile runs only (the headline is a listed workload)")
+        M, N, K = (int(x) for x in args.shape.split(","))
+        head_w = synth.Workload(head_w.index, "q8_shape_m%d_n%d_k%d" % (M, N, K), M, N, K, head_w.outliers)
     log("[bench] preparing %s" % head_w.name)
     head = Operands(torch, q8, head_w, rotate=not args.no_rotate)
     log("[bench] %s: %d rotated copies; timing %d steps after %d warmup"
