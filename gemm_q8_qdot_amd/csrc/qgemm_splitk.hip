@@ -17,6 +17,10 @@
 // workgroups as compute units): per slice it brings in 64 activation rows
 // and 64 weight rows of its k range only.  The split costs about 4 us of
 // fixed reduction work, so it is taken for K >= 8192 only (see splitk_plan).
+// With one slice (S = 1: no workspace, each workgroup stores its tile) the
+// same kernel also serves the plain entries for medium shapes whose 32 x 32
+// tiles would take the one-tile GEMM several rounds of workgroups (see
+// splitk_whole_k).
 //
 //   - Staging: stages of 8 blocks (256 k); a 4-stage ring in LDS (36 KB a
 //     stage) filled by direct global->LDS loads, three stages ahead.  Each
