@@ -218,3 +218,28 @@ def test_header_compiles_as_c_and_links(tmp_path, lib):
     assert int(out["ealign"]) == q8.Q8_EALIGN
     assert int(out["empty"]) == q8.Q8_OK
     assert out["strerror"] == q8.q8_strerror(q8.Q8_ELAUNCH)
+
+
+def _expected_path(M, N, K, cus=256):
+    """The documented dispatch for Q8_0 weights (header, q8_qdot_path), restated."""
+    if M <= 7:
+        return 0
+    staged_tiles = -(-M // 128) * -(-N // 224)
+    if M >= 128 and staged_tiles >= 128 and K * 224 < 2 ** 31:
+        return 2
+    t32 = -(-M // 32) * -(-N // 32)
+    t64 = -(-M // 64) * -(-N // 64)
+    if K * 64 <= 2 ** 31 - 1 and t64 <= 0x7FFFFFFF and 100 * -(-t32 // cus) > 245 * -(-t64 // cus):
+        return 3
+    return 1
+
+
+def test_path_dispatch_rule_over_many_shapes(lib):
+    # The dispatch query follows one rule for every shape (on this host the
+    # library assumes 256 compute units: no device is visible).
+    rng = __import__("numpy").random.default_rng(4242)
+    for _ in range(4000):
+        M = int(rng.integers(1, 3000))
+        N = int(rng.integers(1, 60000))
+        K = 32 * int(rng.integers(1, 2000))
+        assert q8.q8_qdot_path(M, N, K) == _expected_path(M, N, K), (M, N, K)
