@@ -24,7 +24,14 @@
 //     f32 bias pattern, then the 2-op f32 epilogue of ws_pair, the
 //     activation scale broadcast by DPP from one VGPR per chunk (as in the
 //     staged GEMM) instead of sixteen LDS reads per block.
-// Sixteen waves per workgroup (four per SIMD).  Measured on MI355X (M=64,
+// Sixteen waves per workgroup (four per SIMD) while the tiles fit the
+// compute units in one round; with more tiles than compute units, eight
+// waves per workgroup (72 KB of LDS), so two workgroups share a compute unit
+// and the second round of tiles runs beside the first (measured on MI355X,
+// us, sixteen against eight waves: M=16, N=14336, K=4096 19.6 / 17.6; M=8
+// 18.5 / 16.3; M=32 21.5 / 20.1; M=128, N=4096 18.6 / 16.4; M=96 18.1 /
+// 15.9; M=512, N=1024 18.0 / 15.5; Q5_0 weights, M=16, N=14336 20.8 / 19.1;
+// the one-round M=64, N=4096 workload within 1 % either way).  Measured on MI355X (M=64,
 // N=4096, K=4096): each compute unit spends about 2 us bringing in its
 // 256 KB and about 3 us in the epilogue; keeping two chunks in flight per
 // wave (a VGPR double buffer, which fits once the wave index is scalar)
@@ -44,7 +51,8 @@ namespace {
 #define Q8_KS_WAVES 16
 #endif
 
-constexpr int kKsWaves = Q8_KS_WAVES;  // waves per workgroup (K split)
+constexpr int kKsWaves = Q8_KS_WAVES;  // waves per workgroup (K split), one round of tiles
+constexpr int kKsWavesShared = 8;      // more tiles than compute units: two workgroups per unit
 constexpr int kKsBlocks = 4;           // Q8_0 blocks per chunk
 constexpr int kKsSeg = kKsBlocks * kBlock;  // 128 bytes of a row per chunk
 
@@ -353,23 +361,34 @@ hipError_t launch_ks(const int8_t* A, const float* AS, const int8_t* W, const fl
     return hipGetLastError();
 }
 
+// Waves per workgroup for a shape: kKsWaves while its 32 x 32 tiles fit the
+// compute units in one round, else kKsWavesShared (two workgroups per unit).
+template <bool Q5>
+hipError_t launch_ks_any(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
+                         float* C, int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
+    const int64_t tiles = ((int64_t)M + kTile - 1) / kTile * (((int64_t)N + kTile - 1) / kTile);
+    if (tiles > device_cu_count()) {
+        if (P != nullptr) return launch_ks<kKsWavesShared, true, false, Q5>(A, AS, W, WS, C, P, M, N, K, stream);
+        if (ws_t) return launch_ks<kKsWavesShared, false, true, Q5>(A, AS, W, WS, C, P, M, N, K, stream);
+        return launch_ks<kKsWavesShared, false, false, Q5>(A, AS, W, WS, C, P, M, N, K, stream);
+    }
+    if (P != nullptr) return launch_ks<kKsWaves, true, false, Q5>(A, AS, W, WS, C, P, M, N, K, stream);
+    if (ws_t) return launch_ks<kKsWaves, false, true, Q5>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks<kKsWaves, false, false, Q5>(A, AS, W, WS, C, P, M, N, K, stream);
+}
+
 }  // namespace
 
 hipError_t launch_qgemm_ksplit(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                                float* C, int32_t* P, int M, int N, int K, bool ws_t,
                                hipStream_t stream) {
-    if (P != nullptr) return launch_ks<kKsWaves, true, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
-    if (ws_t) return launch_ks<kKsWaves, false, true, false>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_ks<kKsWaves, false, false, false>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks_any<false>(A, AS, W, WS, C, P, M, N, K, ws_t, stream);
 }
 
 hipError_t launch_qgemm_ksplit_q50(const int8_t* A, const float* AS, const uint8_t* W5,
                                    const float* WS, float* C, int32_t* P, int M, int N, int K,
                                    bool ws_t, hipStream_t stream) {
-    const int8_t* W = reinterpret_cast<const int8_t*>(W5);
-    if (P != nullptr) return launch_ks<kKsWaves, true, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
-    if (ws_t) return launch_ks<kKsWaves, false, true, true>(A, AS, W, WS, C, P, M, N, K, stream);
-    return launch_ks<kKsWaves, false, false, true>(A, AS, W, WS, C, P, M, N, K, stream);
+    return launch_ks_any<true>(A, AS, reinterpret_cast<const int8_t*>(W5), WS, C, P, M, N, K, ws_t, stream);
 }
 
 }  // namespace q8

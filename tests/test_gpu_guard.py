@@ -63,6 +63,7 @@ CASES = [
     ("qdot", 1, 130, 16416),      # chunked matvec (rows longer than 16 KiB)
     ("qdot", 3, 1000, 4128),      # small-batch matvec
     ("qdot", 70, 300, 1056),      # K-split MFMA GEMM
+    ("qdot", 100, 3000, 1056),    # K-split MFMA GEMM, two workgroups per compute unit
     ("qdot", 129, 14336, 96),     # LDS-staged MFMA GEMM, ragged M
     ("qdot", 300, 2000, 1056),    # 64 x 64-tile GEMM over all of K, ragged M, N, K
     ("qmma", 1, 1000, 4096),      # matvec with transposed scales
@@ -71,6 +72,7 @@ CASES = [
     ("qmma", 270, 1900, 544),     # 64 x 64-tile GEMM with transposed scales
     ("q50", 1, 1001, 4096),       # Q5_0 matvec
     ("q50", 9, 100, 1056),        # Q5_0 K-split GEMM
+    ("q50", 40, 7000, 1056),      # Q5_0 K-split GEMM, two workgroups per compute unit
     ("q50t", 2, 333, 2048),       # Q5_0 matvec, transposed scales
 ]
 

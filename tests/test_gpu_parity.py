@@ -232,6 +232,42 @@ def test_staged_gemm_shapes(dev, M, N, K):
     _check_partials_sliced(P, A, W, "staged P")
 
 
+# The K-split GEMM with more 32 x 32 tiles than compute units (eight-wave
+# workgroups, two per compute unit): a 16-row decode batch against the
+# 14336-row weight, and ragged M, N, K; Q8_0 and Q5_0 weights, both scale
+# layouts, partials in full.
+KSPLIT_SHARED = [(16, 14336, 1024), (100, 3000, 1056)]
+
+
+@pytest.mark.parametrize("M,N,K", KSPLIT_SHARED)
+def test_ksplit_shared_workgroups(dev, M, N, K):
+    assert q8.q8_qdot_path(M, N, K) == 1
+    assert -(-M // 32) * -(-N // 32) > 256
+    seed = M * 13 + N * 3 + K
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 10.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-4, 1.0)
+    W5 = synth.random_q50(N, K, seed + 4)
+    _say("[parity] K-split, shared workgroups M=%d N=%d K=%d" % (M, N, K))
+    tA, tAS, tW, tWS, tW5 = (_dev(x, dev) for x in (A, AS, W, WS, W5))
+    WST = np.ascontiguousarray(WS.T)
+    C = q8.q8_qdot(tA, tAS, tW, tWS)
+    C2 = q8.q8_qmma(tA, tAS, tW, _dev(WST, dev))
+    C5 = q8.q8_q50_qdot(tA, tAS, tW5, tWS)
+    P = q8.q8_qdot_partials(tA, tW)
+    P5 = q8.q8_q50_partials(tA, tW5)
+    torch.cuda.synchronize()
+    out, mag = oracle.qdot_f64(A, AS, W, WS)
+    _assert_close(C.cpu().numpy(), out, mag, "K-split shared C")
+    out, mag = oracle.qmma_f64(A, AS, W, WST)
+    _assert_close(C2.cpu().numpy(), out, mag, "K-split shared C (qmma)")
+    out, mag = oracle.q50_qdot_f64(A, AS, W5, WS)
+    _assert_close(C5.cpu().numpy(), out, mag, "K-split shared C (Q5_0)")
+    _check_partials_sliced(P, A, W, "K-split shared P")
+    assert np.array_equal(P5.cpu().numpy(), oracle.q50_block_partials(A, W5)), "K-split shared P (Q5_0)"
+
+
 # The 64 x 64-tile GEMM over all of K: the M=512 workload's 8-way N share at
 # its full K, and ragged M, N and K (a partial last stage of blocks).
 WHOLE_K = [(512, 1792, 4096), (300, 2000, 1056), (270, 1900, 544)]
