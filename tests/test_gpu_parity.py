@@ -209,6 +209,32 @@ def test_edge_shapes(dev, M, N, K):
     _check_full(A, AS, W, WS, dev, "edge")
 
 
+# Large extents: one activation row of 128 KiB (eight 16 KiB chunks), 200003
+# short weight rows (many rows per wave), a batch of 50000 rows, and the
+# K-split GEMM over 2048 and 1024 blocks; Q5_0 weights past the 16 Ki values
+# of the decode kernel.
+LARGE = [(1, 64, 131072), (1, 200003, 256), (3, 50000, 512), (9, 40, 65536), (200, 70, 32768)]
+
+
+@pytest.mark.parametrize("M,N,K", LARGE)
+def test_large_extents(dev, M, N, K):
+    seed = M * 7 + N + K // 32
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 10.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-4, 1.0)
+    _check_full(A, AS, W, WS, dev, "large")
+    if K > 16384 and N <= 100:
+        W5 = synth.random_q50(N, K, seed + 4)
+        tA, tAS, tW5, tWS = (_dev(x, dev) for x in (A, AS, W5, WS))
+        C5 = q8.q8_q50_qdot(tA, tAS, tW5, tWS)
+        P5 = q8.q8_q50_partials(tA, tW5)
+        torch.cuda.synchronize()
+        out, mag = oracle.q50_qdot_f64(A, AS, W5, WS)
+        _assert_close(C5.cpu().numpy(), out, mag, "large (Q5_0)")
+        assert np.array_equal(P5.cpu().numpy(), oracle.q50_block_partials(A, W5)), "large (Q5_0) partials"
+
+
 STAGED = [(129, 14336, 96), (136, 14300, 160), (256, 14400, 4128), (512, 14336, 32)]
 
 
