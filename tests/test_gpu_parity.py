@@ -209,6 +209,61 @@ def test_edge_shapes(dev, M, N, K):
     _check_full(A, AS, W, WS, dev, "edge")
 
 
+# Subnormal weight scales (below 2^-126) on every third block, against
+# activation scales of 1e26 (the largest the M >= 8 epilogue's bound covers
+# for such scales, per the header): every path must stay finite and inside
+# the bound.  One row, a batch, the K-split GEMM (one round and shared), the
+# staged GEMM, the 64 x 64-tile GEMM.
+@pytest.mark.parametrize("M,N,K", [(1, 300, 2048), (4, 300, 2048), (9, 300, 2048), (16, 9000, 512),
+                                   (129, 14336, 128), (300, 2000, 256)])
+def test_subnormal_weight_scales(dev, M, N, K):
+    seed = M * 5 + N + K
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 1.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-4, 1.0)
+    KB = K // 32
+    for b in range(0, KB, 3):
+        WS[:, b] = np.float32(1e-40) * np.float32(1 + (b % 7))   # subnormal f32
+        AS[:, b] = np.float32(1e26)
+    assert (WS[:, 0] < np.finfo(np.float32).tiny).all() and (WS[:, 0] > 0).all()
+    _check_full(A, AS, W, WS, dev, "subnormal scales")
+    WST = np.ascontiguousarray(WS.T)
+    C2 = q8.q8_qmma(_dev(A, dev), _dev(AS, dev), _dev(W, dev), _dev(WST, dev))
+    torch.cuda.synchronize()
+    out, mag = oracle.qmma_f64(A, AS, W, WST)
+    _assert_close(C2.cpu().numpy(), out, mag, "subnormal scales (qmma)")
+
+
+# The decode kernels form AS * WS in f32 before the block sum, so subnormal
+# weight scales against activation scales near 1e36 give ordinary products
+# that carry the whole result: a kernel (or a build) that flushed subnormal
+# operands to zero would miss every output (checked on the host: the result
+# with WS flushed fails the bound everywhere).
+@pytest.mark.parametrize("M,N,K", [(1, 300, 2048), (4, 300, 2048), (1, 300, 20480)])
+def test_subnormal_scales_decode_kernels(dev, M, N, K):
+    A = synth.random_i8((M, K), 61 + M)
+    W = synth.random_i8((N, K), 62 + M)
+    AS = (np.float32(1e36) * synth.random_scales((M, K // 32), 63 + M, 0.5, 2.0)).astype(np.float32)
+    WS = (np.float32(1e-40) * synth.random_scales((N, K // 32), 64 + M, 1.0, 10.0)).astype(np.float32)
+    assert (WS < np.finfo(np.float32).tiny).all()
+    out, mag = oracle.qdot_f64(A, AS, W, WS)
+    flushed, _ = oracle.qdot_f64(A, AS, W, np.zeros_like(WS))
+    assert not oracle.within_tolerance(flushed.astype(np.float32), out, mag).any()
+    assert q8.q8_qdot_path(M, N, K) == 0
+    _check_full(A, AS, W, WS, dev, "subnormal scales, decode")
+    tA, tAS, tW = _dev(A, dev), _dev(AS, dev), _dev(W, dev)
+    WST = np.ascontiguousarray(WS.T)
+    C2 = q8.q8_qmma(tA, tAS, tW, _dev(WST, dev))
+    W5 = synth.random_q50(N, K, 65 + M)
+    C5 = q8.q8_q50_qdot(tA, tAS, _dev(W5, dev), _dev(WS, dev))
+    torch.cuda.synchronize()
+    out2, mag2 = oracle.qmma_f64(A, AS, W, WST)
+    _assert_close(C2.cpu().numpy(), out2, mag2, "subnormal scales, decode (qmma)")
+    out5, mag5 = oracle.q50_qdot_f64(A, AS, W5, WS)
+    _assert_close(C5.cpu().numpy(), out5, mag5, "subnormal scales, decode (Q5_0)")
+
+
 # Large extents: one activation row of 128 KiB (eight 16 KiB chunks), 200003
 # short weight rows (many rows per wave), a batch of 50000 rows, and the
 # K-split GEMM over 2048 and 1024 blocks; Q5_0 weights past the 16 Ki values
