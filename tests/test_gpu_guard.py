@@ -1,7 +1,8 @@
 """GPU: every kernel writes exactly its output, nothing around it.
 
 Each case places the output (C f32, or P int32) inside a larger buffer whose
-surrounding words hold a sentinel bit pattern, calls the C-ABI entry with
+surrounding words hold a sentinel bit pattern (at a 4-byte but not 16-byte
+aligned address, the documented minimum), calls the C-ABI entry with
 the interior address, and checks that (a) the words before and after are
 untouched, (b) every output word was written, and (c) the output matches
 the oracle (partials bit for bit, f32 within the contraction's tolerance).
@@ -37,14 +38,19 @@ def _say(msg):
     sys.stdout.flush()
 
 
+# The outputs (C, P, the quantizer's D) need only 4-byte alignment: they
+# start one word past the guard, so no kernel may assume more.
+LEAD = GUARD + 1
+
+
 def _guarded(n, dtype, dev):
-    buf = torch.full((GUARD + n + GUARD,), SENTINEL, dtype=torch.int32, device=dev)
-    return buf, buf[GUARD:GUARD + n].view(dtype)
+    buf = torch.full((LEAD + n + GUARD,), SENTINEL, dtype=torch.int32, device=dev)
+    return buf, buf[LEAD:LEAD + n].view(dtype)
 
 
 def _check_guard(buf, n, what):
     host = buf.cpu().numpy()
-    before, inner, after = host[:GUARD], host[GUARD:GUARD + n], host[GUARD + n:]
+    before, inner, after = host[:LEAD], host[LEAD:LEAD + n], host[LEAD + n:]
     assert (before == SENTINEL).all(), "%s: wrote %d words before the output" % (what, (before != SENTINEL).sum())
     assert (after == SENTINEL).all(), "%s: wrote %d words after the output" % (what, (after != SENTINEL).sum())
     unwritten = int((inner == SENTINEL).sum())
