@@ -235,6 +235,40 @@ def test_subnormal_weight_scales(dev, M, N, K):
     _assert_close(C2.cpu().numpy(), out, mag, "subnormal scales (qmma)")
 
 
+def _dev_offset(x, dev, words=1):
+    # a device copy of x starting `words` 4-byte words past a fresh
+    # allocation's (256-byte aligned) start: 4-byte but not 16-byte aligned
+    flat = torch.zeros(x.size + words, dtype=torch.from_numpy(x[:0]).dtype, device=dev)
+    flat[words:] = torch.from_numpy(np.ascontiguousarray(x).ravel()).to(dev)
+    return flat[words:].view(*x.shape)
+
+
+# Scales and the output at 4-byte (not 16-byte) aligned addresses on every
+# path: the kernels that load scales 16 bytes at a time must fall back to
+# dword loads, and no store may assume more than 4-byte alignment.
+@pytest.mark.parametrize("M,N,K", [(1, 3000, 4096), (4, 300, 2048), (9, 300, 2048), (16, 9000, 512),
+                                   (129, 14336, 128), (300, 2000, 256)])
+def test_misaligned_scales_and_output(dev, M, N, K):
+    seed = M * 3 + N + K
+    A = synth.random_i8((M, K), seed)
+    W = synth.random_i8((N, K), seed + 1)
+    AS = synth.random_scales((M, K // 32), seed + 2, 1e-3, 10.0)
+    WS = synth.random_scales((N, K // 32), seed + 3, 1e-4, 1.0)
+    _say("[parity] misaligned scales and C M=%d N=%d K=%d path=%d" % (M, N, K, q8.q8_qdot_path(M, N, K)))
+    tA, tW = _dev(A, dev), _dev(W, dev)
+    tAS, tWS = _dev_offset(AS, dev), _dev_offset(WS, dev)
+    tWST = _dev_offset(np.ascontiguousarray(WS.T), dev)
+    assert tAS.data_ptr() % 16 != 0 and tWS.data_ptr() % 16 != 0 and tWST.data_ptr() % 16 != 0
+    C = _dev_offset(np.zeros((M, N), np.float32), dev)
+    C2 = _dev_offset(np.zeros((M, N), np.float32), dev, 3)
+    q8.q8_qdot(tA, tAS, tW, tWS, C)
+    q8.q8_qmma(tA, tAS, tW, tWST, C2)
+    torch.cuda.synchronize()
+    out, mag = oracle.qdot_f64(A, AS, W, WS)
+    _assert_close(C.cpu().numpy(), out, mag, "misaligned (qdot)")
+    _assert_close(C2.cpu().numpy(), out, mag, "misaligned (qmma)")
+
+
 # The decode kernels form AS * WS in f32 before the block sum, so subnormal
 # weight scales against activation scales near 1e36 give ordinary products
 # that carry the whole result: a kernel (or a build) that flushed subnormal
