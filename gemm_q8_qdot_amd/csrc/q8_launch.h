@@ -74,6 +74,13 @@ hipError_t launch_qgemm_splitk(const int8_t* A, const float* AS, const int8_t* W
 // no workspace): taken instead of the K-split GEMM where its 64 x 64 tiles
 // need fewer rounds of workgroups (splitk_whole_k).
 bool splitk_whole_k(int M, int N, int K);
+// The LDS-staged GEMM's output tile (qgemm.hip: kBM rows, kStagedTN tiles
+// of kTile columns), for the choice between that kernel and this one.
+constexpr int kStagedTileM = 128;
+constexpr int kStagedTileN = 224;
+// Shapes the staged GEMM would take on which the 64 x 64-tile kernel over
+// all of K is faster.
+bool splitk_over_staged(int M, int N, int K);
 int splitk_whole_k_blocks(int K);
 // The same with the library's file-scope scratch array as the workspace (no
 // allocation); splitk_scratch_capacity() is the largest workspace it stands

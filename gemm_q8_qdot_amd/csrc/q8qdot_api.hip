@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 201;  // 0.2.1: medium GEMMs on 64 x 64 tiles over all of K (path 3)
+constexpr int kVersion = 202;  // 0.2.2: path 3 with two workgroups per CU, also below the staged GEMM
 constexpr int kMatvecMaxM = 7;  // M < 8 -> matvec; the MFMA path needs 8+ rows to pay off
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -34,10 +34,12 @@ int status_of(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ELAUNCH; }
 
 // The block GEMM a Q8_0 shape with M >= 8 takes (q8_qdot_path's numbers):
 // 1 = K-split (32 x 32 tiles), 2 = LDS-staged (128 x 224 tiles), 3 = the
-// 64 x 64-tile ring kernel over all of K (the split-K kernel's one-slice form).
+// 64 x 64-tile ring kernel over all of K (the split-K kernel's one-slice
+// form), which takes over from either where it is faster.
 int gemm_path(int M, int N, int K) {
     const int v = q8::qgemm_variant(M, N, K);
-    return v == 1 && q8::splitk_whole_k(M, N, K) ? 3 : v;
+    if (v == 1) return q8::splitk_whole_k(M, N, K) ? 3 : 1;
+    return q8::splitk_over_staged(M, N, K) ? 3 : v;
 }
 
 // ws_t: WS is the qmma_t form, stored transposed [K/32][N].  split: the

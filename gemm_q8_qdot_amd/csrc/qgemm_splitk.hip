@@ -20,23 +20,28 @@
 // With one slice (S = 1: no workspace, each workgroup stores its tile) the
 // same kernel also serves the plain entries for medium shapes whose 32 x 32
 // tiles would take the one-tile GEMM several rounds of workgroups (see
-// splitk_whole_k).
+// splitk_whole_k), and for shapes of one or two rounds of the staged GEMM's
+// tiles on which it is faster (see splitk_over_staged).  Launches with more
+// workgroups than compute units take a half-width form (4-block stages,
+// 8 waves, a 72 KB ring) so that two workgroups share a unit.
 //
-//   - Staging: stages of 8 blocks (256 k); a 4-stage ring in LDS (36 KB a
-//     stage) filled by direct global->LDS loads, three stages ahead.  Each
-//     stage is 48 wave-wide load instructions (16 for the activation rows,
-//     16 for the weight rows, 8 + 8 for the scales), three per wave, so every
-//     wave waits for the same number of loads.  Row segments are stored with
-//     their 16-byte chunks permuted (chunk c of row r at c ^ (r mod 16)) so
-//     that the MFMA fragment reads are free of bank conflicts; the
-//     permutation is applied by choosing which global chunk each lane loads.
-//   - Math: 16 waves; wave w computes the 32 x 32 sub-tile w mod 4 on blocks
-//     2 (w / 4) and 2 (w / 4) + 1 of every stage: one v_mfma_i32_32x32x32_i8
+//   - Staging: stages of 8 blocks (256 k; 4 in the half-width form); a
+//     4-stage ring in LDS (36 KB a stage; 18 KB) filled by direct
+//     global->LDS loads, three stages ahead.  Each stage is 48 wave-wide
+//     load instructions (16 for the activation rows, 16 for the weight rows,
+//     8 + 8 for the scales; half of each in the half-width form), three per
+//     wave, so every wave waits for the same number of loads.  Row segments
+//     are stored with their 16-byte chunks permuted (chunk c of row r at
+//     c ^ (r mod 16); 128-byte rows: c ^ swz(r)) so that the MFMA fragment
+//     reads are free of bank conflicts; the permutation is applied by
+//     choosing which global chunk each lane loads.
+//   - Math: 16 waves (8); wave w computes the 32 x 32 sub-tile w mod 4 on
+//     blocks 2 (w / 4) and 2 (w / 4) + 1 of every stage: one v_mfma_i32_32x32x32_i8
 //     per block (one Q8_0 block), seeded with the f32 bias pattern, and the
 //     2-operation epilogue of ws_pair with the activation scale broadcast by
 //     DPP (see qgemm.hip).
-//   - Reduction: the four waves of a sub-tile are summed in LDS in wave
-//     order.  With S > 1 each workgroup writes its 64 x 64 partial tile to
+//   - Reduction: the four (two) waves of a sub-tile are summed in LDS in
+//     wave order.  With S > 1 each workgroup writes its 64 x 64 partial tile to
 //     the workspace, and the last of the tile's S workgroups to finish (an
 //     atomic counter per tile) adds the S partial tiles in slice order
 //     (0, 1, ..., S - 1, so the result does not depend on which finished
@@ -47,16 +52,15 @@
 #include "q8_device.h"
 #include "q8_launch.h"
 
+#include <type_traits>
+
 namespace q8 {
 namespace {
 
 constexpr int kSkM = 64;                          // activation rows per tile
 constexpr int kSkN = 64;                          // weight rows per tile
-constexpr int kSkSB = 8;                          // Q8_0 blocks per stage
-constexpr int kSkSeg = kSkSB * kBlock;            // 256 bytes of a row per stage
+constexpr int kSkSB = 8;                          // blocks per stage, one workgroup per CU
 constexpr int kSkRing = 4;                        // stages in LDS
-constexpr int kSkWaves = 16;
-constexpr int kSkThreads = kSkWaves * kWave;
 constexpr int kSkTileFloats = kSkM * kSkN;        // one partial tile
 // Workspace layout: one 32-bit counter per output tile in a fixed area at
 // the start (so that calls of any shape sharing a workspace find their
@@ -64,22 +68,51 @@ constexpr int kSkTileFloats = kSkM * kSkN;        // one partial tile
 constexpr int kSkMaxTiles = 1024;
 constexpr size_t kSkCounterBytes = kSkMaxTiles * sizeof(unsigned);
 
-struct SkStage {
-    int8_t a[kSkM * kSkSeg];          // [row][16 chunks of 16 B], permuted
-    int8_t w[kSkN * kSkSeg];
-    float as[kSkM * kSkSB];           // [row][block]
-    float ws[kSkN * kSkSB];           // [row][block]; transposed scales: [block][column]
+// Stage width SB (Q8_0 blocks per stage): 8 (16 waves, a 144 KB ring: one
+// workgroup per compute unit) or 4 (8 waves, a 72 KB ring: two workgroups
+// share a compute unit, for launches with more workgroups than units).
+// Either way every wave computes one 32 x 32 sub-tile on two blocks of each
+// stage and issues three loads per stage.
+template <int SB>
+struct SkShape {
+    static constexpr int kSeg = SB * kBlock;          // bytes of a row per stage
+    static constexpr int kChunks = kSeg / 16;         // 16-byte chunks of a row segment
+    static constexpr int kWaves = 2 * SB;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kJobRows = kWave / kChunks;  // rows of one 16-byte-per-lane load
 };
-static_assert(sizeof(SkStage) == 36864, "stage layout");
-constexpr size_t kSkSmem = sizeof(SkStage) * kSkRing;
-static_assert(kSkSmem <= 160 * 1024, "LDS budget");
-static_assert((size_t)kSkWaves * 16 * kWave * sizeof(float) <= kSkSmem, "reduction area");
+
+template <int SB>
+struct SkStage {
+    int8_t a[kSkM * SkShape<SB>::kSeg];  // [row][chunks], permuted
+    int8_t w[kSkN * SkShape<SB>::kSeg];
+    float as[kSkM * SB];                 // [row][block]
+    float ws[kSkN * SB];                 // [row][block]; transposed scales: [block][column]
+};
+template <int SB>
+constexpr size_t sk_ring_bytes() { return sizeof(SkStage<SB>) * kSkRing; }
+static_assert(sizeof(SkStage<8>) == 36864 && sizeof(SkStage<4>) == 18432, "stage layout");
+static_assert(sk_ring_bytes<8>() <= 160 * 1024 && 2 * sk_ring_bytes<4>() <= 160 * 1024, "LDS budget");
+static_assert((size_t)SkShape<8>::kWaves * 16 * kWave * sizeof(float) <= sk_ring_bytes<8>() &&
+              (size_t)SkShape<4>::kWaves * 16 * kWave * sizeof(float) <= sk_ring_bytes<4>(), "reduction area");
+static_assert(kSkM / SkShape<8>::kJobRows == SkShape<8>::kWaves &&
+              kSkM / SkShape<4>::kJobRows == SkShape<4>::kWaves, "one operand job per wave");
+
+// Chunk c of row r sits at physical chunk c ^ perm(r): sixteen consecutive
+// rows read at one logical chunk hit sixteen distinct 16-byte bank groups,
+// so the MFMA fragment reads are free of bank conflicts (256-byte rows:
+// r mod 16; 128-byte rows: swz).
+template <int SB>
+__device__ __forceinline__ int sk_perm(int r) {
+    if constexpr (SB == 8) return r & 15;
+    else return swz(r);
+}
 
 // WST: weight scales stored [K/32][N] (qmma_t).  S > 1: cnt (one counter per
 // tile) and part (tiles x S partial tiles) are the workspace; cnt_clear (or
 // null) is a counter area this kernel zero-fills for a later call.
-template <bool PARTIALS, bool WST>
-__global__ void __launch_bounds__(kSkThreads, 1)
+template <bool PARTIALS, bool WST, int SB>
+__global__ void __launch_bounds__(SkShape<SB>::kThreads, SB == kSkSB ? 1 : 2)
 qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
                     float* __restrict__ C, int32_t* __restrict__ P, int M, int N, int K,
@@ -92,7 +125,8 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         for (int k = blockIdx.x * kWave + threadIdx.x; k < kSkMaxTiles; k += gridDim.x * kWave)
             __hip_atomic_store(&cnt_clear[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    SkStage* ring = reinterpret_cast<SkStage*>(sk_smem);
+    using Sh = SkShape<SB>;
+    SkStage<SB>* ring = reinterpret_cast<SkStage<SB>*>(sk_smem);
     __shared__ int last_flag;
 
     // The 8 XCDs take workgroups round-robin: consecutive ids (the S slices
@@ -107,7 +141,7 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const int KB = K / kBlock;
     const int kb_lo = slice * slice_blocks;
     const int kb_hi = min(KB, kb_lo + slice_blocks);
-    const int nst = (kb_hi - kb_lo + kSkSB - 1) / kSkSB;
+    const int nst = (kb_hi - kb_lo + SB - 1) / SB;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
@@ -125,35 +159,37 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const v4i dWS = make_desc(PARTIALS ? nullptr : WS + (WST ? (int64_t)j0 : (int64_t)j0 * KB),
                               WST ? ((int64_t)KB * N - j0) * 4 : (int64_t)rows_w * KB * 4);
 
-    // Load jobs of stage st (three per wave).  Operand job q (wave q): rows
-    // 4q .. 4q + 3; lane l fills physical chunk l % 16 of row 4q + l / 16,
-    // i.e. loads logical chunk (l % 16) ^ (row % 16).  Scale job e: rows
-    // 8e .. 8e + 7, block l % 8 of row 8e + l / 8 ([row][block]); transposed
-    // weight scales: block e, column l ([block][column]).  A chunk or block
-    // past the slice (or past K) reads nothing and lands as zeros; so does a
+    // Load jobs of stage st (three per wave).  Operand job q (wave q): the
+    // kJobRows rows from kJobRows q; lane l fills physical chunk
+    // l % kChunks of row kJobRows q + l / kChunks, i.e. loads the logical
+    // chunk (l % kChunks) ^ perm(row).  Scale job e (waves below SB: the
+    // activation scales; the others: the weight scales): rows
+    // (64 / SB) e + l / SB, block l % SB ([row][block]); transposed weight
+    // scales: block e, column l ([block][column]).  A chunk or block past
+    // the slice (or past K) reads nothing and lands as zeros; so does a
     // stage past the last one (its ring slot is not read again).
-    const int op_row = 4 * wv + lane / 16;
-    const int op_chunk = (lane % 16) ^ (op_row & 15);
+    const int op_row = Sh::kJobRows * wv + lane / Sh::kChunks;
+    const int op_chunk = (lane % Sh::kChunks) ^ sk_perm<SB>(op_row);
     const int op_voff = op_row * K + 16 * op_chunk;
-    const int sc_row = 8 * (wv & 7) + lane / 8;
-    const int sc_blk = lane % 8;
+    const int sc_job = wv < SB ? wv : wv - SB;
+    const int sc_row = kSkM / SB * sc_job + lane / SB;
+    const int sc_blk = lane % SB;
     auto issue_stage = [&](int st) {
-        SkStage& sg = ring[st % kSkRing];
-        const int kbs = kb_lo + st * kSkSB;  // first block of the stage
+        SkStage<SB>& sg = ring[st % kSkRing];
+        const int kbs = kb_lo + st * SB;  // first block of the stage
         const bool in = st < nst;
         const int vo = (in && kbs + op_chunk / 2 < kb_hi) ? op_voff : kNoRead;
-        dma16(dA, lds_addr(&sg.a[wv * 4 * kSkSeg]), vo, kbs * kBlock);
-        dma16(dW, lds_addr(&sg.w[wv * 4 * kSkSeg]), vo, kbs * kBlock);
-        if (wv < 8) {
+        dma16(dA, lds_addr(&sg.a[wv * Sh::kJobRows * Sh::kSeg]), vo, kbs * kBlock);
+        dma16(dW, lds_addr(&sg.w[wv * Sh::kJobRows * Sh::kSeg]), vo, kbs * kBlock);
+        if (wv < SB) {
             const bool ok = !PARTIALS && in && kbs + sc_blk < kb_hi;
-            dma4(dAS, lds_addr(&sg.as[wv * kWave]), ok ? (sc_row * KB + kbs + sc_blk) * 4 : kNoRead, 0);
+            dma4(dAS, lds_addr(&sg.as[sc_job * kWave]), ok ? (sc_row * KB + kbs + sc_blk) * 4 : kNoRead, 0);
         } else if constexpr (WST) {
-            const int e = wv - 8;
-            const bool ok = !PARTIALS && in && kbs + e < kb_hi;
-            dma4(dWS, lds_addr(&sg.ws[e * kWave]), ok ? ((kbs + e) * N + lane) * 4 : kNoRead, 0);
+            const bool ok = !PARTIALS && in && kbs + sc_job < kb_hi;
+            dma4(dWS, lds_addr(&sg.ws[sc_job * kWave]), ok ? ((kbs + sc_job) * N + lane) * 4 : kNoRead, 0);
         } else {
             const bool ok = !PARTIALS && in && kbs + sc_blk < kb_hi;
-            dma4(dWS, lds_addr(&sg.ws[(wv - 8) * kWave]), ok ? (sc_row * KB + kbs + sc_blk) * 4 : kNoRead, 0);
+            dma4(dWS, lds_addr(&sg.ws[sc_job * kWave]), ok ? (sc_row * KB + kbs + sc_blk) * 4 : kNoRead, 0);
         }
     };
 
@@ -169,8 +205,8 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int c = 2 * (2 * kq + t) + half;  // logical chunk of block 2 kq + t
-        frag_a[t] = a_row * kSkSeg + 16 * (c ^ (a_row & 15));
-        frag_w[t] = w_row * kSkSeg + 16 * (c ^ (w_row & 15));
+        frag_a[t] = a_row * Sh::kSeg + 16 * (c ^ sk_perm<SB>(a_row));
+        frag_w[t] = w_row * Sh::kSeg + 16 * (c ^ sk_perm<SB>(w_row));
     }
 
     v16i bias;
@@ -182,13 +218,13 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
     auto compute_stage = [&](int st) {
-        const SkStage& sg = ring[st % kSkRing];
-        const int kbs = kb_lo + st * kSkSB + 2 * kq;
+        const SkStage<SB>& sg = ring[st % kSkRing];
+        const int kbs = kb_lo + st * SB + 2 * kq;
         float2 ws2 = make_float2(0.0f, 0.0f), as2 = make_float2(0.0f, 0.0f);
         if constexpr (!PARTIALS) {
-            as2 = *reinterpret_cast<const float2*>(&sg.as[as_row * kSkSB + 2 * kq]);
+            as2 = *reinterpret_cast<const float2*>(&sg.as[as_row * SB + 2 * kq]);
             if constexpr (WST) ws2 = make_float2(sg.ws[(2 * kq) * kSkN + w_row], sg.ws[(2 * kq + 1) * kSkN + w_row]);
-            else ws2 = *reinterpret_cast<const float2*>(&sg.ws[w_row * kSkSB + 2 * kq]);
+            else ws2 = *reinterpret_cast<const float2*>(&sg.ws[w_row * SB + 2 * kq]);
         }
         const float wsv[2] = {ws2.x, ws2.y};
         const float asv[2] = {as2.x, as2.y};
@@ -256,7 +292,7 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
         for (int st = 0; st < nst; ++st) {
             for (int t = 0; t < 2; ++t) {
-                const int b = kb_lo + st * kSkSB + 2 * kq + t;
+                const int b = kb_lo + st * SB + 2 * kq + t;
                 if (b >= kb_hi) break;
                 const int ko = b * kBlock + 16 * half;
                 const v4i af = ia < M ? load16(A + (int64_t)ia * K + ko) : v4i{0, 0, 0, 0};
@@ -273,8 +309,8 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         }
     }
 
-    // The four waves of each sub-tile, summed in wave order (kq = 0..3).
-    float* red = reinterpret_cast<float*>(sk_smem);  // [16 waves][16][64]
+    // The waves of each sub-tile, summed in wave order (kq = 0, 1, ...).
+    float* red = reinterpret_cast<float*>(sk_smem);  // [waves][16][64]
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[(wv * 16 + r) * kWave + lane] = acc[r];
     __syncthreads();
@@ -283,9 +319,8 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float s = red[(wv * 16 + r) * kWave + lane];
-            s += red[((wv + 4) * 16 + r) * kWave + lane];
-            s += red[((wv + 8) * 16 + r) * kWave + lane];
-            s += red[((wv + 12) * 16 + r) * kWave + lane];
+#pragma unroll
+            for (int k = 1; k < Sh::kWaves / 4; ++k) s += red[((wv + 4 * k) * 16 + r) * kWave + lane];
             tot[r] = s;
         }
     }
@@ -401,6 +436,33 @@ bool splitk_whole_k(int M, int N, int K) {
     return 100 * r32 > 245 * r64;
 }
 
+// Shapes the LDS-staged GEMM would take (at least 128 of its 128 x 224
+// tiles) on which this kernel, two workgroups per compute unit, is faster.
+// The staged GEMM runs in rounds of one workgroup per unit, a round costing
+// about as much as a full one even when partly filled; this kernel's time
+// grows with its 64 x 64 tiles per unit (~0.07 us per tile per K/32 = 128
+// blocks, i.e. ~18 us per tile per unit at K = 4096).  Measured on MI355X
+// (us, staged against this kernel, K = 4096 unless noted; 64 x 64 tiles):
+// 256 x 14336 (896) 77.1 / 69.0; 128 x 28672 (896) 78.2 / 73.3; 130 x 14336
+// (672) 72.8 / 53.6; 256 x 16384 (1024) 80.8 / 72.1; 1024 x 4096 (1024)
+// 78.6 / 70.8; 2048 x 4096 (2048, two staged rounds) 149.6 / 140.3;
+// 256 x 14336 x 8192 139.9 / 123.3; K = 1024: 256 x 14336 25.9 / 26.2,
+// 1024 x 4096 25.9 / 25.2.  And the other way: 320 x 14336 (1120) 79.1 /
+// 85.2; 384 x 14336 (1344) 81.2 / 100.2; 1536 x 4096 (1536) 87.4 / 109.6;
+// 512 x 14336 (1792) 90.9 / 123.8; 640 x 14336 (2240, two rounds) 151.5 /
+// 148.4; 768 x 14336 (2688, two rounds) 151.3 / 171.0.  Rule: this kernel
+// when its tiles number at most 4.1 per unit per staged round.
+bool splitk_over_staged(int M, int N, int K) {
+    if (M < 8 || N < 1 || K < kBlock || (int64_t)K * kSkM > INT32_MAX) return false;
+    const int64_t cus = device_cu_count();
+    const int64_t t64 = ((int64_t)M + kSkM - 1) / kSkM * (((int64_t)N + kSkN - 1) / kSkN);
+    const int64_t ts = ((int64_t)M + kStagedTileM - 1) / kStagedTileM *
+                       (((int64_t)N + kStagedTileN - 1) / kStagedTileN);
+    if (t64 > 0x7FFFFFFF) return false;
+    const int64_t rounds = (ts + cus - 1) / cus;
+    return 10 * t64 <= 41 * cus * rounds;
+}
+
 int splitk_whole_k_blocks(int K) { return (K / kBlock + kSkSB - 1) / kSkSB * kSkSB; }
 
 namespace {
@@ -413,18 +475,31 @@ hipError_t launch_splitk(const int8_t* A, const float* AS, const int8_t* W, cons
     const int64_t tiles_n = ((int64_t)N + kSkN - 1) / kSkN;
     const int64_t total = tiles_m * tiles_n * S;
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    auto launch = [&](auto kern) -> hipError_t {
+    // More workgroups than compute units: the 8-wave form with its 72 KB
+    // ring, so that two workgroups share a unit and one's loads run under
+    // the other's math.
+    const bool shared = total > device_cu_count();
+    auto launch = [&](auto kern, auto sb_const) -> hipError_t {
+        constexpr int SB = decltype(sb_const)::value;
+        constexpr size_t smem = sk_ring_bytes<SB>();
         static std::atomic<uint64_t> lds_set[2][2] = {{{0}, {0}}, {{0}, {0}}};
-        const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)kSkSmem,
+        const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)smem,
                                              lds_set[P != nullptr][ws_t]);
         if (e != hipSuccess) return e;
-        kern<<<dim3((unsigned)total), kSkThreads, kSkSmem, stream>>>(
+        kern<<<dim3((unsigned)total), SkShape<SB>::kThreads, smem, stream>>>(
             A, AS, W, WS, C, P, M, N, K, (int)tiles_m, S, slice_blocks, part, cnt, cnt_clear);
         return hipGetLastError();
     };
-    if (P != nullptr) return launch(qgemm_splitk_kernel<true, false>);
-    if (ws_t) return launch(qgemm_splitk_kernel<false, true>);
-    return launch(qgemm_splitk_kernel<false, false>);
+    using Wide = std::integral_constant<int, kSkSB>;
+    using Narrow = std::integral_constant<int, kSkSB / 2>;
+    if (shared) {
+        if (P != nullptr) return launch(qgemm_splitk_kernel<true, false, Narrow::value>, Narrow{});
+        if (ws_t) return launch(qgemm_splitk_kernel<false, true, Narrow::value>, Narrow{});
+        return launch(qgemm_splitk_kernel<false, false, Narrow::value>, Narrow{});
+    }
+    if (P != nullptr) return launch(qgemm_splitk_kernel<true, false, Wide::value>, Wide{});
+    if (ws_t) return launch(qgemm_splitk_kernel<false, true, Wide::value>, Wide{});
+    return launch(qgemm_splitk_kernel<false, false, Wide::value>, Wide{});
 }
 
 // ---- The no-allocation form: the workspace is this file-scope device

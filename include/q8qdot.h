@@ -216,9 +216,12 @@ int q8_qdot_noalloc(const int8_t *A, const float *AS, const int8_t *W, const flo
  * and N), 3 = one workgroup per 64 x 64 output tile over all of K, staged
  * through an LDS ring (medium shapes: too few 128 x 224 tiles to fill the
  * chip, but so many 32 x 32 tiles that one workgroup per 64 x 64 tile needs
- * far fewer rounds of workgroups; the kernel of q8_qdot_ws's split form,
- * with one slice and no workspace).  The debug entry q8_qdot_partials takes
- * the same kernel.  Q5_0 weights take 0 or 1.  Q8_EINVAL for bad shapes.
+ * far fewer rounds of workgroups; also shapes with one or two rounds of
+ * 128 x 224 tiles but at most about four 64 x 64 tiles per compute unit
+ * per round, where two of its workgroups per unit beat the staged GEMM;
+ * the kernel of q8_qdot_ws's split form, with one slice and no workspace).
+ * The debug entry q8_qdot_partials takes the same kernel.  Q5_0 weights
+ * take 0 or 1.  Q8_EINVAL for bad shapes.
  */
 int q8_qdot_path(int M, int N, int K);
 

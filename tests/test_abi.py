@@ -67,7 +67,8 @@ def test_path_dispatch(lib):
     assert q8.q8_qdot_path(8, 4096, 4096) == 1
     assert q8.q8_qdot_path(64, 4096, 4096) == 1
     assert q8.q8_qdot_path(512, 14336, 4096) == 2
-    assert q8.q8_qdot_path(129, 14336, 96) == 2
+    assert q8.q8_qdot_path(385, 14336, 96) == 2
+    assert q8.q8_qdot_path(129, 14336, 96) == 3   # below the staged GEMM's rule
     assert q8.q8_qdot_path(128, 449, 512) == 1
     # many 32 x 32 tiles but too few 128 x 224 ones: 64 x 64 tiles over all of K
     # (on a 256-compute-unit part: 896 against 224 tiles, 4 rounds against 1)
@@ -225,11 +226,13 @@ def _expected_path(M, N, K, cus=256):
     if M <= 7:
         return 0
     staged_tiles = -(-M // 128) * -(-N // 224)
-    if M >= 128 and staged_tiles >= 128 and K * 224 < 2 ** 31:
-        return 2
     t32 = -(-M // 32) * -(-N // 32)
     t64 = -(-M // 64) * -(-N // 64)
-    if K * 64 <= 2 ** 31 - 1 and t64 <= 0x7FFFFFFF and 100 * -(-t32 // cus) > 245 * -(-t64 // cus):
+    ring_ok = K * 64 <= 2 ** 31 - 1 and t64 <= 0x7FFFFFFF
+    if M >= 128 and staged_tiles >= 128 and K * 224 < 2 ** 31:
+        # the ring kernel where it has at most 4.1 tiles per unit per staged round
+        return 3 if ring_ok and 10 * t64 <= 41 * cus * -(-staged_tiles // cus) else 2
+    if ring_ok and 100 * -(-t32 // cus) > 245 * -(-t64 // cus):
         return 3
     return 1
 

@@ -32,7 +32,8 @@ CASES = [
     ("qdot", 4, 2048, 4096, 0),
     ("qdot", 64, 1024, 4096, 1),
     ("qdot", 16, 14336, 1024, 1),
-    ("qdot", 256, 14336, 1024, 2),
+    ("qdot", 385, 14336, 1024, 2),
+    ("qdot", 256, 14336, 1024, 3),
     ("qdot", 300, 2000, 1056, 3),
     ("qmma", 64, 1024, 4096, 1),
     ("q50", 1, 4096, 4096, None),

@@ -49,9 +49,10 @@ def _replay_and_compare(g, out, eager, what):
 
 
 # matvec (M = 1, a small batch, rows over 16 KiB), K-split GEMM, staged GEMM,
-# 64 x 64-tile GEMM over all of K, the empty sum (K = 0)
+# 64 x 64-tile GEMM over all of K (one workgroup per unit, and two), the
+# empty sum (K = 0)
 SHAPES = [(1, 4096, 4096), (4, 2000, 4096), (1, 300, 16416), (64, 1024, 1024),
-          (256, 14336, 512), (300, 2000, 1056), (3, 77, 0)]
+          (385, 14336, 512), (300, 2000, 1056), (256, 14336, 512), (3, 77, 0)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

@@ -70,12 +70,15 @@ CASES = [
     ("qdot", 3, 1000, 4128),      # small-batch matvec
     ("qdot", 70, 300, 1056),      # K-split MFMA GEMM
     ("qdot", 100, 3000, 1056),    # K-split MFMA GEMM, two workgroups per compute unit
-    ("qdot", 129, 14336, 96),     # LDS-staged MFMA GEMM, ragged M
+    ("qdot", 385, 14336, 96),     # LDS-staged MFMA GEMM, ragged M
+    ("qdot", 129, 14336, 96),     # 64 x 64-tile GEMM where the staged one would be slower
     ("qdot", 300, 2000, 1056),    # 64 x 64-tile GEMM over all of K, ragged M, N, K
+    ("qdot", 520, 2100, 1056),    # 64 x 64-tile GEMM, two workgroups per compute unit
     ("qmma", 1, 1000, 4096),      # matvec with transposed scales
     ("qmma", 5, 1000, 2080),      # small batch with transposed scales
-    ("qmma", 130, 14300, 128),    # staged GEMM with transposed scales
+    ("qmma", 390, 14300, 128),    # staged GEMM with transposed scales
     ("qmma", 270, 1900, 544),     # 64 x 64-tile GEMM with transposed scales
+    ("qmma", 520, 2100, 544),     # the same, two workgroups per compute unit
     ("q50", 1, 1001, 4096),       # Q5_0 matvec
     ("q50", 9, 100, 1056),        # Q5_0 K-split GEMM
     ("q50", 40, 7000, 1056),      # Q5_0 K-split GEMM, two workgroups per compute unit

@@ -184,7 +184,7 @@ def test_small_batch(dev, M, N, K):
 
 # one row, a small batch, the K-split GEMM, the LDS-staged GEMM, the
 # 64 x 64-tile GEMM over all of K
-@pytest.mark.parametrize("M,N,K", [(1, 3000, 4096), (4, 3000, 4096), (64, 512, 2048), (256, 14336, 256),
+@pytest.mark.parametrize("M,N,K", [(1, 3000, 4096), (4, 3000, 4096), (64, 512, 2048), (385, 14336, 256),
                                    (300, 2000, 1024)])
 def test_cancelling_half_blocks(dev, M, N, K):
     A, AS, W, WS = synth.cancelling_blocks(M, N, K, 880 + M)
@@ -213,9 +213,9 @@ def test_edge_shapes(dev, M, N, K):
 # activation scales of 1e26 (the largest the M >= 8 epilogue's bound covers
 # for such scales, per the header): every path must stay finite and inside
 # the bound.  One row, a batch, the K-split GEMM (one round and shared), the
-# staged GEMM, the 64 x 64-tile GEMM.
+# staged GEMM, the 64 x 64-tile GEMM (one workgroup per unit and shared).
 @pytest.mark.parametrize("M,N,K", [(1, 300, 2048), (4, 300, 2048), (9, 300, 2048), (16, 9000, 512),
-                                   (129, 14336, 128), (300, 2000, 256)])
+                                   (385, 14336, 128), (300, 2000, 256), (129, 14336, 128)])
 def test_subnormal_weight_scales(dev, M, N, K):
     seed = M * 5 + N + K
     A = synth.random_i8((M, K), seed)
@@ -247,7 +247,7 @@ def _dev_offset(x, dev, words=1):
 # path: the kernels that load scales 16 bytes at a time must fall back to
 # dword loads, and no store may assume more than 4-byte alignment.
 @pytest.mark.parametrize("M,N,K", [(1, 3000, 4096), (4, 300, 2048), (9, 300, 2048), (16, 9000, 512),
-                                   (129, 14336, 128), (300, 2000, 256)])
+                                   (385, 14336, 128), (300, 2000, 256), (129, 14336, 128)])
 def test_misaligned_scales_and_output(dev, M, N, K):
     seed = M * 3 + N + K
     A = synth.random_i8((M, K), seed)
@@ -324,7 +324,7 @@ def test_large_extents(dev, M, N, K):
         assert np.array_equal(P5.cpu().numpy(), oracle.q50_block_partials(A, W5)), "large (Q5_0) partials"
 
 
-STAGED = [(129, 14336, 96), (136, 14300, 160), (256, 14400, 4128), (512, 14336, 32)]
+STAGED = [(385, 14336, 96), (390, 14300, 160), (384, 14400, 2080), (512, 14336, 32)]
 
 
 @pytest.mark.parametrize("M,N,K", STAGED)
@@ -385,7 +385,11 @@ def test_ksplit_shared_workgroups(dev, M, N, K):
 
 # The 64 x 64-tile GEMM over all of K: the M=512 workload's 8-way N share at
 # its full K, and ragged M, N and K (a partial last stage of blocks).
-WHOLE_K = [(512, 1792, 4096), (300, 2000, 1056), (270, 1900, 544)]
+# the last four have more 64 x 64 tiles than compute units (two workgroups
+# share a unit: the 8-wave form of the kernel); the last two are shapes the
+# staged GEMM would take but is slower on
+WHOLE_K = [(512, 1792, 4096), (300, 2000, 1056), (270, 1900, 544), (512, 4096, 1024), (520, 2100, 1056),
+           (129, 14336, 96), (136, 14300, 160)]
 
 
 @pytest.mark.parametrize("M,N,K", WHOLE_K)
@@ -411,10 +415,10 @@ def test_whole_k_gemm_shapes(dev, M, N, K):
 
 
 # one row, the K-split GEMM (M = 9, and M = 129 with few tiles), the
-# LDS-staged GEMM (M = 129 with N = 14336), the 64 x 64-tile GEMM over all
-# of K (M = 300, N = 2000)
-@pytest.mark.parametrize("M,N,K", [(1, 70, 1024), (9, 70, 1024), (129, 70, 1024), (129, 14336, 256),
-                                   (300, 2000, 1024)])
+# LDS-staged GEMM (M = 385 with N = 14336), the 64 x 64-tile GEMM over all
+# of K (M = 300, N = 2000; M = 129, N = 14336 with two workgroups per unit)
+@pytest.mark.parametrize("M,N,K", [(1, 70, 1024), (9, 70, 1024), (129, 70, 1024), (385, 14336, 256),
+                                   (300, 2000, 1024), (129, 14336, 256)])
 def test_extreme_bytes_and_scales(dev, M, N, K):
     A = np.full((M, K), -128, np.int8)
     W = synth.random_i8((N, K), 77)
@@ -436,7 +440,7 @@ def test_extreme_bytes_and_scales(dev, M, N, K):
         WS[3:40, b] = np.float32(2.0 ** e)
         AS[:, b] = np.float32(2.0 ** -e)
     if M > 1:
-        assert q8.q8_qdot_path(M, N, K) == (2 if N == 14336 else 3 if N == 2000 else 1)
+        assert q8.q8_qdot_path(M, N, K) == (2 if M == 385 else 3 if N in (2000, 14336) else 1)
     _check_full(A, AS, W, WS, dev, "extreme")
     WST = np.ascontiguousarray(WS.T)
     C2 = q8.q8_qmma(_dev(A, dev), _dev(AS, dev), _dev(W, dev), _dev(WST, dev))

@@ -118,8 +118,9 @@ SHAPES = [
     # scales beside the scale tile), several tiles per share, ragged shares
     (7, 500, 16384), (4, 3000, 8192), (2, 14336, 4096), (6, 40000, 1024),
     (9, 37, 96), (33, 100, 4096), (127, 300, 4160), (64, 4099, 128),    # K-split
-    (512, 7168, 1024),                                                  # staged, 16-byte scales
-    (512, 7170, 1024), (256, 14400, 4128), (136, 14300, 160),           # staged, dword scales
+    (512, 14336, 1024),                                                 # staged, 16-byte scales
+    (390, 14302, 1024), (384, 14400, 2080), (392, 14300, 160),          # staged, dword scales
+    (512, 7168, 1024), (136, 14300, 160),                               # 64 x 64 tiles, shared units
 ]
 
 

@@ -4,7 +4,8 @@ The shapes are drawn once from a fixed seed so that each dispatch regime is
 reached several times with sizes nobody picked by hand: one activation row,
 small batches (2..7 rows), the K-split GEMM (few output tiles), the
 LDS-staged GEMM (M >= 128 and many tiles, short K) and the 64 x 64-tile GEMM
-over all of K (medium M x N, short K); N and K/32 are
+over all of K (medium M x N, short K; and, two workgroups per compute unit,
+shapes the staged GEMM would take but is slower on); N and K/32 are
 ragged (any value; one activation row up to 600 blocks, past the 16 KiB
 rows of the one-row kernels).  Each case runs q8_qdot, q8_qmma (the same
 scales transposed), q8_q50_qdot and q8_q50_qmma (Q5_0 weights) and both
@@ -42,9 +43,12 @@ def _draw_cases(per_regime=6, seed=20261202):
         M, K = int(rng.integers(8, 601)), 32 * int(rng.integers(1, 513))
         cases.append((M, int(rng.integers(1, max(2, min(600, MAX_MNK // (M * K))) + 1)), K))
     for _ in range(per_regime):       # many tiles: the LDS-staged GEMM, short K
+        # (one round of 128 x 224 tiles, and more than 4.1 tiles of 64 x 64
+        # per compute unit, so the staged GEMM is the faster)
         M = int(rng.integers(128, 601))
-        n_min = 224 * (-(-128 // -(-M // 128)))
-        cases.append((M, int(rng.integers(n_min, n_min + 3000)), 32 * int(rng.integers(1, 9))))
+        n_lo = max(224 * (-(-128 // -(-M // 128))), 64 * (-(-1050 // -(-M // 64))))
+        n_hi = 224 * (256 // -(-M // 128))
+        cases.append((M, int(rng.integers(n_lo, n_hi + 1)), 32 * int(rng.integers(1, 9))))
     for _ in range(per_regime):       # 520..1000 tiles of 32 x 32 (three or four
         # rounds on 256 compute units), one round of 64 x 64 tiles, too few
         # 128 x 224 tiles: the 64 x 64-tile GEMM over all of K, short K
@@ -53,6 +57,13 @@ def _draw_cases(per_regime=6, seed=20261202):
         nt = int(rng.integers(-(-520 // mt), 1000 // mt + 1))
         N = 32 * nt - int(rng.integers(0, 32))
         cases.append((M, N, 32 * int(rng.integers(1, 9))))
+    for _ in range(per_regime):       # shapes the staged GEMM would take with at
+        # most 4.1 tiles of 64 x 64 per compute unit: the 64 x 64-tile GEMM,
+        # two workgroups per unit, short K
+        M = int(rng.integers(128, 601))
+        n_lo = 224 * (-(-128 // -(-M // 128)))
+        n_hi = min(224 * (256 // -(-M // 128)), 64 * (1049 // -(-M // 64)))
+        cases.append((M, int(rng.integers(n_lo, n_hi + 1)), 32 * int(rng.integers(1, 9))))
     return cases
 
 
@@ -127,8 +138,8 @@ def test_cases_reach_every_path():
     # each regime of the draw lands on its dispatch path (0 matvec,
     # 1 K-split GEMM, 2 LDS-staged GEMM, 3 64 x 64-tile GEMM over all of K)
     paths = [q8.q8_qdot_path(M, N, K) for M, N, K in CASES]
-    per = len(CASES) // 5
+    per = len(CASES) // 6
     assert paths[:2 * per] == [0] * (2 * per)
     assert paths[2 * per:3 * per] == [1] * per
-    assert paths[3 * per:4 * per] == [2] * per
-    assert paths[4 * per:] == [3] * per, CASES[4 * per:]
+    assert paths[3 * per:4 * per] == [2] * per, CASES[3 * per:4 * per]
+    assert paths[4 * per:] == [3] * (2 * per), CASES[4 * per:]
