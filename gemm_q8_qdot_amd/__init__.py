@@ -30,7 +30,7 @@ Q8_ERANGE = -5
 # Every symbol include/q8qdot.h declares.
 EXPORTS = ("q8_qdot", "q8_qdot_stream", "q8_qmma", "q8_qdot_partials", "q8_qdot_path",
            "q8_qdot_ws_size", "q8_qdot_ws", "q8_qmma_ws", "q8_qdot_ws_partials", "q8_qdot_noalloc",
-           "q8_q50_qdot", "q8_q50_qmma", "q8_q50_partials",
+           "q8_q50_qdot", "q8_q50_qmma", "q8_q50_partials", "q8_q50_path",
            "q8_quantize", "q8_strerror", "q8_version")
 
 _lock = threading.Lock()
@@ -84,6 +84,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         lib.q8_qdot_ws_partials.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         lib.q8_qdot_path.restype = ci
         lib.q8_qdot_path.argtypes = [ci, ci, ci]
+        lib.q8_q50_path.restype = ci
+        lib.q8_q50_path.argtypes = [ci, ci, ci]
         lib.q8_quantize.restype = ci
         lib.q8_quantize.argtypes = [vp, vp, vp, ci, ci, vp]
         lib.q8_strerror.restype = ctypes.c_char_p
@@ -390,6 +392,15 @@ def q8_qdot_path(M: int, N: int, K: int) -> int:
     st = load().q8_qdot_path(M, N, K)
     if st < 0:
         raise Q8Error(st, "q8_qdot_path")
+    return st
+
+
+def q8_q50_path(M: int, N: int, K: int) -> int:
+    """Q5_0 weights (16-byte aligned): 0 = Q5_0 matvec, 1 = K-split MFMA GEMM, 3 = 64 x 64-tile
+    ring GEMM decoding each stage in LDS."""
+    st = load().q8_q50_path(M, N, K)
+    if st < 0:
+        raise Q8Error(st, "q8_q50_path")
     return st
 
 

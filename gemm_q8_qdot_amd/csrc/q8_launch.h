@@ -81,6 +81,15 @@ constexpr int kStagedTileN = 224;
 // Shapes the staged GEMM would take on which the 64 x 64-tile kernel over
 // all of K is faster.
 bool splitk_over_staged(int M, int N, int K);
+// Whether the kernel over all of K has more 64 x 64 tiles than compute
+// units (its two-workgroups-per-unit form).
+bool splitk_shared(int M, int N);
+// The same kernel over all of K for Q5_0 weights (W5: 20 bytes per 32
+// values), decoding each stage's blocks into LDS once (the two-workgroups-
+// per-unit form only).
+hipError_t launch_qgemm_splitk_q50(const int8_t* A, const float* AS, const uint8_t* W5,
+                                   const float* WS, float* C, int32_t* P, int M, int N, int K,
+                                   bool ws_t, hipStream_t stream);
 int splitk_whole_k_blocks(int K);
 // The same with the library's file-scope scratch array as the workspace (no
 // allocation); splitk_scratch_capacity() is the largest workspace it stands

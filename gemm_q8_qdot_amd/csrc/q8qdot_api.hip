@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 202;  // 0.2.2: path 3 with two workgroups per CU, also below the staged GEMM
+constexpr int kVersion = 203;  // 0.2.3: Q5_0 weights on the 64 x 64-tile ring GEMM (q8_q50_path)
 constexpr int kMatvecMaxM = 7;  // M < 8 -> matvec; the MFMA path needs 8+ rows to pay off
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -183,6 +183,18 @@ Q8_API int q8_qdot_noalloc(const int8_t* A, const float* AS, const int8_t* W, co
                                                      static_cast<hipStream_t>(stream)));
 }
 
+// Q5_0 weights at M >= 8: the 64 x 64-tile ring GEMM (each stage's blocks
+// decoded once in LDS) for the shapes whose Q8_0 GEMM is the staged one or
+// that kernel -- there is no staged form for Q5_0 -- and that have more of
+// its tiles than compute units (two workgroups per unit: with one, its
+// per-stage decode and second barrier made it slower than the K-split GEMM),
+// when its whole-piece loads of the weight rows are 16-byte aligned (K/32 a
+// multiple of 4, and a 16-byte aligned W5, checked by the caller); else the
+// K-split GEMM.
+bool q50_ring(int M, int N, int K) {
+    return M > kMatvecMaxM && (K / 32) % 4 == 0 && gemm_path(M, N, K) >= 2 && q8::splitk_shared(M, N);
+}
+
 // Q5_0 weights: W5 is [N][K/32 * 20] bytes, 4-byte aligned (dword loads).
 static int run_q50(const int8_t* A, const float* AS, const uint8_t* W5, const float* WS, float* C,
             int32_t* P, int M, int N, int K, bool ws_t, hipStream_t stream) {
@@ -211,8 +223,13 @@ static int run_q50(const int8_t* A, const float* AS, const uint8_t* W5, const fl
     } else if (!aligned(AS, 4) || !aligned(WS, 4) || !aligned(C, 4)) {
         return Q8_EALIGN;
     }
-    hipError_t e = matvec ? q8::launch_matvec_q50(A, AS, W5, WS, C, P, M, N, K, ws_t, stream)
-                          : q8::launch_qgemm_ksplit_q50(A, AS, W5, WS, C, P, M, N, K, ws_t, stream);
+    hipError_t e;
+    if (matvec)
+        e = q8::launch_matvec_q50(A, AS, W5, WS, C, P, M, N, K, ws_t, stream);
+    else if (q50_ring(M, N, K) && aligned(W5, 16))
+        e = q8::launch_qgemm_splitk_q50(A, AS, W5, WS, C, P, M, N, K, ws_t, stream);
+    else
+        e = q8::launch_qgemm_ksplit_q50(A, AS, W5, WS, C, P, M, N, K, ws_t, stream);
     return status_of(e);
 }
 
@@ -263,6 +280,14 @@ Q8_API const char* q8_strerror(int status) {
         case Q8_ELAUNCH: return "HIP runtime rejected the kernel launch";
         default: return "unknown status";
     }
+}
+
+Q8_API int q8_q50_path(int M, int N, int K) {
+    const int st = check_shape(M, N, K);
+    if (st != Q8_OK) return st;
+    if (M <= kMatvecMaxM && q8::matvec_q50_fits(K) && (int64_t)N * (K / 32) * 20 < INT32_MAX - (1 << 20))
+        return 0;
+    return q50_ring(M, N, K) ? 3 : 1;
 }
 
 Q8_API int q8_version(void) { return kVersion; }

@@ -82,19 +82,52 @@ struct SkShape {
     static constexpr int kJobRows = kWave / kChunks;  // rows of one 16-byte-per-lane load
 };
 
-template <int SB>
+// Q5_0 weights (Q5): the ring holds each stage's raw 20-byte blocks
+// ([row][SB blocks]); after the stage lands the workgroup decodes them once
+// into a signed-byte tile laid out like the activation tile (one area,
+// reused every stage), and a 1 KB spare area takes the loads of waves that
+// have no weight piece to fetch.
+constexpr int kQ5Bytes = 20;  // qh word + 16 nibble bytes per 32 values
+template <int SB, bool Q5>
 struct SkStage {
-    int8_t a[kSkM * SkShape<SB>::kSeg];  // [row][chunks], permuted
-    int8_t w[kSkN * SkShape<SB>::kSeg];
-    float as[kSkM * SB];                 // [row][block]
-    float ws[kSkN * SB];                 // [row][block]; transposed scales: [block][column]
+    int8_t a[kSkM * SkShape<SB>::kSeg];                       // [row][chunks], permuted
+    int8_t w[kSkN * (Q5 ? SB * kQ5Bytes : SkShape<SB>::kSeg)];  // Q5: raw blocks
+    float as[kSkM * SB];                                      // [row][block]
+    float ws[kSkN * SB];  // [row][block]; transposed scales: [block][column]
 };
-template <int SB>
-constexpr size_t sk_ring_bytes() { return sizeof(SkStage<SB>) * kSkRing; }
-static_assert(sizeof(SkStage<8>) == 36864 && sizeof(SkStage<4>) == 18432, "stage layout");
-static_assert(sk_ring_bytes<8>() <= 160 * 1024 && 2 * sk_ring_bytes<4>() <= 160 * 1024, "LDS budget");
-static_assert((size_t)SkShape<8>::kWaves * 16 * kWave * sizeof(float) <= sk_ring_bytes<8>() &&
-              (size_t)SkShape<4>::kWaves * 16 * kWave * sizeof(float) <= sk_ring_bytes<4>(), "reduction area");
+template <int SB, bool Q5>
+constexpr size_t sk_ring_bytes() {
+    return sizeof(SkStage<SB, Q5>) * kSkRing + (Q5 ? kSkN * SkShape<SB>::kSeg + 1024 : 0);
+}
+static_assert(sizeof(SkStage<8, false>) == 36864 && sizeof(SkStage<4, false>) == 18432 &&
+              sizeof(SkStage<8, true>) == 30720 && sizeof(SkStage<4, true>) == 15360, "stage layout");
+static_assert(sk_ring_bytes<8, false>() <= 160 * 1024 && 2 * sk_ring_bytes<4, false>() <= 160 * 1024 &&
+              sk_ring_bytes<8, true>() <= 160 * 1024 && 2 * sk_ring_bytes<4, true>() <= 160 * 1024,
+              "LDS budget");
+static_assert((size_t)SkShape<8>::kWaves * 16 * kWave * sizeof(float) <= sk_ring_bytes<8, true>() &&
+              (size_t)SkShape<4>::kWaves * 16 * kWave * sizeof(float) <= sk_ring_bytes<4, true>() &&
+              (size_t)SkShape<8>::kWaves * 16 * kWave * sizeof(float) <= sk_ring_bytes<8, false>() &&
+              (size_t)SkShape<4>::kWaves * 16 * kWave * sizeof(float) <= sk_ring_bytes<4, false>(),
+              "reduction area");
+// Raw Q5_0 pieces of a stage: 16 bytes per lane, whole pieces per row.
+static_assert((8 * kQ5Bytes) % 16 == 0 && (4 * kQ5Bytes) % 16 == 0, "Q5_0 row segments in 16-byte pieces");
+static_assert(kSkN * 8 * kQ5Bytes / 16 <= SkShape<8>::kWaves * kWave &&
+              kSkN * 4 * kQ5Bytes / 16 <= SkShape<4>::kWaves * kWave, "one Q5_0 piece job per wave at most");
+
+// Signed bytes of half h (values 16 h .. 16 h + 15) of a Q5_0 block: code
+// nibble | (bit of qh) << 4, value code - 16 ("Quantized built-ins and
+// formats", section "Q5_0").  The byte permute turns each bit into the
+// value's sign bits (selector 0x0C gives 0x00, 0x0D gives 0xFF).
+__device__ __forceinline__ v4i q50_half(uint32_t qh, const uint32_t (&qs)[4], int h) {
+    v4i out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t nib = (qs[d] >> (4 * h)) & 0x0F0F0F0Fu;
+        const uint32_t sel = 0x0D0D0D0Du - spread4(__builtin_amdgcn_ubfe(qh, 16 * h + 4 * d, 4));
+        out[d] = (int)((__builtin_amdgcn_perm(0u, 0u, sel) & 0xF0F0F0F0u) | nib);
+    }
+    return out;
+}
 static_assert(kSkM / SkShape<8>::kJobRows == SkShape<8>::kWaves &&
               kSkM / SkShape<4>::kJobRows == SkShape<4>::kWaves, "one operand job per wave");
 
@@ -111,7 +144,8 @@ __device__ __forceinline__ int sk_perm(int r) {
 // WST: weight scales stored [K/32][N] (qmma_t).  S > 1: cnt (one counter per
 // tile) and part (tiles x S partial tiles) are the workspace; cnt_clear (or
 // null) is a counter area this kernel zero-fills for a later call.
-template <bool PARTIALS, bool WST, int SB>
+// Q5: W holds Q5_0 blocks (20 bytes per 32 values, rows of K/32 blocks).
+template <bool PARTIALS, bool WST, int SB, bool Q5>
 __global__ void __launch_bounds__(SkShape<SB>::kThreads, SB == kSkSB ? 1 : 2)
 qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                     const int8_t* __restrict__ W, const float* __restrict__ WS,
@@ -126,7 +160,10 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             __hip_atomic_store(&cnt_clear[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     using Sh = SkShape<SB>;
-    SkStage<SB>* ring = reinterpret_cast<SkStage<SB>*>(sk_smem);
+    SkStage<SB, Q5>* ring = reinterpret_cast<SkStage<SB, Q5>*>(sk_smem);
+    // Q5: the decoded weight tile and the spare load target, after the ring
+    int8_t* dec = reinterpret_cast<int8_t*>(sk_smem) + sizeof(SkStage<SB, Q5>) * kSkRing;
+    int8_t* spare = dec + kSkN * Sh::kSeg;
     __shared__ int last_flag;
 
     // The 8 XCDs take workgroups round-robin: consecutive ids (the S slices
@@ -152,7 +189,8 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 
     // Descriptors of this tile's rows: reads past them return 0.
     const v4i dA = make_desc(A + (int64_t)i0 * K, (int64_t)rows_a * K);
-    const v4i dW = make_desc(W + (int64_t)j0 * K, (int64_t)rows_w * K);
+    const int64_t w_pitch = Q5 ? (int64_t)KB * kQ5Bytes : K;  // bytes per weight row
+    const v4i dW = make_desc(W + (int64_t)j0 * w_pitch, (int64_t)rows_w * w_pitch);
     const v4i dAS = make_desc(PARTIALS ? nullptr : AS + (int64_t)i0 * KB, (int64_t)rows_a * KB * 4);
     // Transposed weight scales: from column j0 to the end of the array
     // (columns past the tile meet zero weight rows and are never stored).
@@ -171,16 +209,30 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
     const int op_row = Sh::kJobRows * wv + lane / Sh::kChunks;
     const int op_chunk = (lane % Sh::kChunks) ^ sk_perm<SB>(op_row);
     const int op_voff = op_row * K + 16 * op_chunk;
+    constexpr int kQ5RowPieces = SB * kQ5Bytes / 16;            // 10 or 5
+    constexpr int q5_jobs = kSkN * kQ5RowPieces / kWave;         // 10 or 5 waves load pieces
+    const int q5_row = (wv * kWave + lane) / kQ5RowPieces;
+    const int q5_part = (wv * kWave + lane) % kQ5RowPieces;
+    const int q5_voff = q5_row * KB * kQ5Bytes + 16 * q5_part;
     const int sc_job = wv < SB ? wv : wv - SB;
     const int sc_row = kSkM / SB * sc_job + lane / SB;
     const int sc_blk = lane % SB;
     auto issue_stage = [&](int st) {
-        SkStage<SB>& sg = ring[st % kSkRing];
+        SkStage<SB, Q5>& sg = ring[st % kSkRing];
         const int kbs = kb_lo + st * SB;  // first block of the stage
         const bool in = st < nst;
         const int vo = (in && kbs + op_chunk / 2 < kb_hi) ? op_voff : kNoRead;
         dma16(dA, lds_addr(&sg.a[wv * Sh::kJobRows * Sh::kSeg]), vo, kbs * kBlock);
-        dma16(dW, lds_addr(&sg.w[wv * Sh::kJobRows * Sh::kSeg]), vo, kbs * kBlock);
+        if constexpr (Q5) {
+            // piece 64 wv + lane of the stage's raw rows ([row][SB * 20 bytes]):
+            // row q5_row, bytes 16 q5_part ..; pieces whose first byte lies
+            // past the slice read nothing
+            const bool real = wv < q5_jobs;
+            const int v5 = (real && in && kbs + q5_part * 16 / kQ5Bytes < kb_hi) ? q5_voff : kNoRead;
+            dma16(dW, lds_addr(real ? (void*)&sg.w[wv * 1024] : (void*)spare), v5, kbs * kQ5Bytes);
+        } else {
+            dma16(dW, lds_addr(&sg.w[wv * Sh::kJobRows * Sh::kSeg]), vo, kbs * kBlock);
+        }
         if (wv < SB) {
             const bool ok = !PARTIALS && in && kbs + sc_blk < kb_hi;
             dma4(dAS, lds_addr(&sg.as[sc_job * kWave]), ok ? (sc_row * KB + kbs + sc_blk) * 4 : kNoRead, 0);
@@ -217,8 +269,24 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
+    // Q5: decode the stage's raw weight blocks into the signed-byte tile
+    // (laid out like the activation tile).  Lane item 64 wv + lane takes
+    // half item % 2 of block (item / 2) % SB of row item / (2 SB): the
+    // workgroup's lanes cover the stage exactly once.  Neighbouring lanes
+    // read neighbouring 20-byte blocks (distinct banks), and the writes of
+    // a wave fill 1 KB of whole permuted rows.
+    auto decode_stage = [&](int st) {
+        const SkStage<SB, Q5>& sg = ring[st % kSkRing];
+        const int item = wv * kWave + lane;
+        const int r = item / (2 * SB), bb = (item / 2) % SB, h = item & 1;
+        const uint32_t* wd = reinterpret_cast<const uint32_t*>(sg.w + r * (SB * kQ5Bytes) + kQ5Bytes * bb);
+        const uint32_t qs[4] = {wd[1], wd[2], wd[3], wd[4]};
+        *reinterpret_cast<v4i*>(dec + r * Sh::kSeg + 16 * ((2 * bb + h) ^ sk_perm<SB>(r))) =
+            q50_half(wd[0], qs, h);
+    };
+
     auto compute_stage = [&](int st) {
-        const SkStage<SB>& sg = ring[st % kSkRing];
+        const SkStage<SB, Q5>& sg = ring[st % kSkRing];
         const int kbs = kb_lo + st * SB + 2 * kq;
         float2 ws2 = make_float2(0.0f, 0.0f), as2 = make_float2(0.0f, 0.0f);
         if constexpr (!PARTIALS) {
@@ -233,7 +301,7 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
             const int b = kbs + t;
             if (b >= kb_hi) break;  // wave-uniform
             const v4i af = *reinterpret_cast<const v4i*>(sg.a + frag_a[t]);
-            const v4i wf = *reinterpret_cast<const v4i*>(sg.w + frag_w[t]);
+            const v4i wf = *reinterpret_cast<const v4i*>((Q5 ? dec : sg.w) + frag_w[t]);
             const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, bias, 0, 0, 0);
             if constexpr (PARTIALS) {
                 const int j = j0 + w_row;
@@ -270,6 +338,13 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
         else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         if (st > 0) issue_stage(st - 1 + kSkRing);
+        if constexpr (Q5) {
+            // every wave's decoded bytes are in LDS before any wave reads
+            // them (no vmcnt wait: the later stages' loads stay in flight)
+            decode_stage(st);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+        }
         compute_stage(st);
     }
     // Every load (the ring's trailing stages included) has landed before
@@ -296,7 +371,17 @@ qgemm_splitk_kernel(const int8_t* __restrict__ A, const float* __restrict__ AS,
                 if (b >= kb_hi) break;
                 const int ko = b * kBlock + 16 * half;
                 const v4i af = ia < M ? load16(A + (int64_t)ia * K + ko) : v4i{0, 0, 0, 0};
-                const v4i wf = jw < N ? load16(W + (int64_t)jw * K + ko) : v4i{0, 0, 0, 0};
+                v4i wf = {0, 0, 0, 0};
+                if (jw < N) {
+                    if constexpr (Q5) {
+                        const int8_t* blk = W + (int64_t)jw * w_pitch + (int64_t)b * kQ5Bytes;
+                        const v4i q = load16_a4(blk + 4);
+                        const uint32_t qs[4] = {(uint32_t)q.x, (uint32_t)q.y, (uint32_t)q.z, (uint32_t)q.w};
+                        wf = q50_half(*reinterpret_cast<const uint32_t*>(blk), qs, half);
+                    } else {
+                        wf = load16(W + (int64_t)jw * K + ko);
+                    }
+                }
                 const v16i d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, zero, 0, 0, 0);
                 const float ws = jw < N ? (WST ? WS[(int64_t)b * N + jw] : WS[(int64_t)jw * KB + b]) : 0.0f;
 #pragma unroll
@@ -463,10 +548,16 @@ bool splitk_over_staged(int M, int N, int K) {
     return 10 * t64 <= 41 * cus * rounds;
 }
 
+bool splitk_shared(int M, int N) {
+    const int64_t t64 = ((int64_t)M + kSkM - 1) / kSkM * (((int64_t)N + kSkN - 1) / kSkN);
+    return t64 > device_cu_count();
+}
+
 int splitk_whole_k_blocks(int K) { return (K / kBlock + kSkSB - 1) / kSkSB * kSkSB; }
 
 namespace {
 
+template <bool Q5>
 hipError_t launch_splitk(const int8_t* A, const float* AS, const int8_t* W, const float* WS,
                          float* C, int32_t* P, int M, int N, int K, bool ws_t, int S,
                          int slice_blocks, unsigned* cnt, float* part, unsigned* cnt_clear,
@@ -477,11 +568,12 @@ hipError_t launch_splitk(const int8_t* A, const float* AS, const int8_t* W, cons
     if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     // More workgroups than compute units: the 8-wave form with its 72 KB
     // ring, so that two workgroups share a unit and one's loads run under
-    // the other's math.
-    const bool shared = total > device_cu_count();
+    // the other's math.  Q5_0 weights always take that form (they are
+    // dispatched here only for such launches).
+    const bool shared = Q5 || total > device_cu_count();
     auto launch = [&](auto kern, auto sb_const) -> hipError_t {
         constexpr int SB = decltype(sb_const)::value;
-        constexpr size_t smem = sk_ring_bytes<SB>();
+        constexpr size_t smem = sk_ring_bytes<SB, Q5>();
         static std::atomic<uint64_t> lds_set[2][2] = {{{0}, {0}}, {{0}, {0}}};
         const hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), (int)smem,
                                              lds_set[P != nullptr][ws_t]);
@@ -493,13 +585,16 @@ hipError_t launch_splitk(const int8_t* A, const float* AS, const int8_t* W, cons
     using Wide = std::integral_constant<int, kSkSB>;
     using Narrow = std::integral_constant<int, kSkSB / 2>;
     if (shared) {
-        if (P != nullptr) return launch(qgemm_splitk_kernel<true, false, Narrow::value>, Narrow{});
-        if (ws_t) return launch(qgemm_splitk_kernel<false, true, Narrow::value>, Narrow{});
-        return launch(qgemm_splitk_kernel<false, false, Narrow::value>, Narrow{});
+        if (P != nullptr) return launch(qgemm_splitk_kernel<true, false, Narrow::value, Q5>, Narrow{});
+        if (ws_t) return launch(qgemm_splitk_kernel<false, true, Narrow::value, Q5>, Narrow{});
+        return launch(qgemm_splitk_kernel<false, false, Narrow::value, Q5>, Narrow{});
     }
-    if (P != nullptr) return launch(qgemm_splitk_kernel<true, false, Wide::value>, Wide{});
-    if (ws_t) return launch(qgemm_splitk_kernel<false, true, Wide::value>, Wide{});
-    return launch(qgemm_splitk_kernel<false, false, Wide::value>, Wide{});
+    if constexpr (!Q5) {
+        if (P != nullptr) return launch(qgemm_splitk_kernel<true, false, Wide::value, false>, Wide{});
+        if (ws_t) return launch(qgemm_splitk_kernel<false, true, Wide::value, false>, Wide{});
+        return launch(qgemm_splitk_kernel<false, false, Wide::value, false>, Wide{});
+    }
+    return hipErrorInvalidValue;  // not reached
 }
 
 // ---- The no-allocation form: the workspace is this file-scope device
@@ -536,8 +631,8 @@ hipError_t launch_qgemm_splitk(const int8_t* A, const float* AS, const int8_t* W
                                int slice_blocks, void* workspace, hipStream_t stream) {
     unsigned* cnt = static_cast<unsigned*>(workspace);
     float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kSkCounterBytes);
-    return launch_splitk(A, AS, W, WS, C, P, M, N, K, ws_t, S, slice_blocks, cnt, part, nullptr,
-                         stream);
+    return launch_splitk<false>(A, AS, W, WS, C, P, M, N, K, ws_t, S, slice_blocks, cnt, part, nullptr,
+                                stream);
 }
 
 size_t splitk_scratch_capacity() { return kSkCounterBytes + kSkScratchParts; }
@@ -554,8 +649,15 @@ hipError_t launch_qgemm_splitk_scratch(const int8_t* A, const float* AS, const i
     unsigned* cnt = reinterpret_cast<unsigned*>(base + (e & 1) * kSkCounterBytes);
     unsigned* clear = reinterpret_cast<unsigned*>(base + ((e + 1) & 1) * kSkCounterBytes);
     float* part = reinterpret_cast<float*>(base + 2 * kSkCounterBytes);
-    return launch_splitk(A, AS, W, WS, C, nullptr, M, N, K, ws_t, S, slice_blocks, cnt, part,
-                         clear, stream);
+    return launch_splitk<false>(A, AS, W, WS, C, nullptr, M, N, K, ws_t, S, slice_blocks, cnt, part,
+                                clear, stream);
+}
+
+hipError_t launch_qgemm_splitk_q50(const int8_t* A, const float* AS, const uint8_t* W5,
+                                   const float* WS, float* C, int32_t* P, int M, int N, int K,
+                                   bool ws_t, hipStream_t stream) {
+    return launch_splitk<true>(A, AS, reinterpret_cast<const int8_t*>(W5), WS, C, P, M, N, K, ws_t, 1,
+                               splitk_whole_k_blocks(K), nullptr, nullptr, nullptr, stream);
 }
 
 }  // namespace q8

@@ -127,9 +127,13 @@ int q8_qmma(const int8_t *A, const float *AS, const int8_t *W, const float *WST,
  * rows that fits in LDS beside the weight staging areas (up to 7 rows of
  * K <= 8192, 6 of 12288, 5 of 14336, 4 of 16384) is taken in one pass that
  * reads the weights once, larger ones one activation row per pass
- * (q8_q50_partials: always one row per pass).  Anything else runs the
- * K-split MFMA GEMM (for which 32 * K, and with WST (K/32) * N * 4, must be
- * below 2^31, else Q8_ERANGE).  q8_q50_partials: P[i][j][b] =
+ * (q8_q50_partials: always one row per pass).  Anything else runs an MFMA
+ * GEMM (for which 32 * K, and with WST (K/32) * N * 4, must be below 2^31,
+ * else Q8_ERANGE): the 64 x 64-tile ring GEMM, decoding each stage's blocks
+ * once in LDS, for shapes whose Q8_0 dispatch (q8_qdot_path) is 2 or 3 and
+ * that have more 64 x 64 output tiles than the GPU has compute units, when
+ * K/32 is a multiple of 4 and W5 is 16-byte aligned; else the K-split GEMM.
+ * q8_q50_path reports which.  q8_q50_partials: P[i][j][b] =
  * sum over the block of A * (q - 16), int32 [M][N][K/32].
  */
 int q8_q50_qdot(const int8_t *A, const float *AS, const uint8_t *W5, const float *WS,
@@ -138,6 +142,14 @@ int q8_q50_qmma(const int8_t *A, const float *AS, const uint8_t *W5, const float
                 float *C, int M, int N, int K, void *stream);
 int q8_q50_partials(const int8_t *A, const uint8_t *W5, int32_t *P, int M, int N, int K,
                     void *stream);
+
+/*
+ * The kernel the Q5_0 entries take for a shape, with a 16-byte aligned W5:
+ * 0 = Q5_0 matvec, 1 = K-split MFMA GEMM, 3 = 64 x 64-tile ring GEMM (as
+ * described above; a W5 that is only 4-byte aligned takes 1 instead of 3).
+ * Q8_EINVAL for bad shapes.
+ */
+int q8_q50_path(int M, int N, int K);
 
 /*
  * Debug entry: P[i][j][b] = the int32 block sum of the qdot_t definition,

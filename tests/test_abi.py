@@ -80,6 +80,33 @@ def test_path_dispatch(lib):
     assert lib.q8_qdot_path(-1, 1, 32) == q8.Q8_EINVAL
 
 
+def test_q50_path_dispatch(lib):
+    # Q5_0 weights: matvec below 8 rows (K <= 16384), the ring GEMM where the
+    # Q8_0 dispatch is the staged or the ring GEMM, its 64 x 64 tiles outnumber
+    # the compute units and K/32 is a multiple of 4, else the K-split GEMM
+    assert q8.q8_q50_path(1, 14336, 4096) == 0
+    assert q8.q8_q50_path(7, 4096, 16384) == 0
+    assert q8.q8_q50_path(3, 4096, 16416) == 1        # rows over 16 KiB: one row per grid row
+    assert q8.q8_q50_path(64, 4096, 4096) == 1
+    assert q8.q8_q50_path(512, 14336, 4096) == 3      # staged for Q8_0
+    assert q8.q8_q50_path(512, 4096, 4096) == 3
+    assert q8.q8_q50_path(512, 1792, 4096) == 1       # one round of 64 x 64 tiles
+    assert q8.q8_q50_path(520, 2100, 1056) == 1       # K/32 = 33
+    assert lib.q8_q50_path(1, 1, 33) == q8.Q8_EINVAL
+    rng = __import__("numpy").random.default_rng(4243)
+    for _ in range(2000):
+        M = int(rng.integers(1, 3000))
+        N = int(rng.integers(1, 60000))
+        K = 32 * int(rng.integers(1, 600))
+        want = _expected_path(M, N, K)
+        if M <= 7:
+            want = 0 if K <= 16384 and N * (K // 32) * 20 < 2 ** 31 - 1 - 2 ** 20 else 1
+        else:
+            t64 = -(-M // 64) * -(-N // 64)
+            want = 3 if want >= 2 and (K // 32) % 4 == 0 and t64 > 256 else 1
+        assert q8.q8_q50_path(M, N, K) == want, (M, N, K)
+
+
 BAD_SHAPES = [(1, 1, 31), (1, 1, -32), (-1, 4, 32), (4, -1, 32), (2, 2, 48)]
 
 

@@ -82,6 +82,8 @@ CASES = [
     ("q50", 1, 1001, 4096),       # Q5_0 matvec
     ("q50", 9, 100, 1056),        # Q5_0 K-split GEMM
     ("q50", 40, 7000, 1056),      # Q5_0 K-split GEMM, two workgroups per compute unit
+    ("q50", 600, 2000, 1152),     # Q5_0 ring GEMM
+    ("q50t", 520, 2100, 1024),    # Q5_0 ring GEMM, two workgroups per compute unit, transposed scales
     ("q50t", 2, 333, 2048),       # Q5_0 matvec, transposed scales
 ]
 

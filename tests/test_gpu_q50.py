@@ -5,8 +5,10 @@ Bar: int32 partials bit-exact; f32 within ``1e-5 * sum_b |AS*WS*P| + 1e-6``.
 Weights are seeded uniform bytes (every byte pattern is a valid Q5_0
 block), so all 32 codes and all qh bit patterns occur.  Shapes reach the
 matvec (M < 8, K <= 16384: one activation row, a batch staged in LDS, or a
-batch too large for LDS taken a row at a time) and the K-split GEMM
-(everything else),
+batch too large for LDS taken a row at a time), the 64 x 64-tile ring GEMM
+(shapes whose Q8_0 GEMM is the staged or the ring one and whose 64 x 64
+tiles outnumber the compute units, with K/32 a multiple of 4 and an aligned
+weight array) and the K-split GEMM (everything else),
 blocks per row not a multiple of 4 (rows that start 4- but not 16-byte
 aligned), ragged M and N, and a weight array that starts 4 bytes past a
 16-byte boundary.
@@ -99,6 +101,31 @@ def test_q50_shapes(dev, M, N, K):
     _check(A, AS, W5, WS, dev, "shape")
 
 
+# The ring GEMM (two workgroups per compute unit): shapes whose Q8_0
+# dispatch is the ring GEMM (520 x 2100, 512 x 4096, 600 x 2000, 129 x 14336)
+# and the staged one (385 x 14336); ragged M and N, one to 36 stages.
+RING = [(520, 2100, 1024), (512, 4096, 512), (600, 2000, 1152), (129, 14336, 128),
+        (385, 14336, 128), (520, 2100, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", RING)
+def test_q50_ring_gemm_shapes(dev, M, N, K):
+    assert q8.q8_q50_path(M, N, K) == 3
+    A, AS, W5, WS = _case(M, N, K, 5500 + M + N + K)
+    _check(A, AS, W5, WS, dev, "ring")
+
+
+def test_q50_ring_fallbacks(dev):
+    # shapes the ring GEMM would take, run on the K-split GEMM: K/32 not a
+    # multiple of 4, and a weight array only 4-byte aligned
+    assert q8.q8_q50_path(520, 2100, 1056) == 1
+    A, AS, W5, WS = _case(520, 2100, 1056, 5600)
+    _check(A, AS, W5, WS, dev, "ring shape, K/32 = 33")
+    assert q8.q8_q50_path(520, 2100, 1024) == 3
+    A, AS, W5, WS = _case(520, 2100, 1024, 5601)
+    _check(A, AS, W5, WS, dev, "ring shape, misaligned", misalign=True)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 200, 4096), (16, 200, 1056)])
 def test_q50_misaligned_weights(dev, M, N, K):
     A, AS, W5, WS = _case(M, N, K, 6100 + M)
@@ -124,3 +151,21 @@ def test_q50_extreme_codes(dev):
         AS[:, b] = np.float32(2.0 ** -e)
     _check(A, AS, W5, WS, dev, "huge weight scales")
     _check(A[:1], AS[:1], W5, WS, dev, "huge weight scales (matvec)")
+
+
+def test_q50_ring_extreme_codes(dev):
+    # the same extremes on the ring GEMM (M = 520, N = 2100, K = 256), whose
+    # non-finite fallback decodes the weight blocks straight from memory
+    M, N, K = 520, 2100, 256
+    assert q8.q8_q50_path(M, N, K) == 3
+    A = np.where(np.arange(K)[None, :] % 2 == 0, -128, 127).astype(np.int8).repeat(M, 0)
+    W5 = synth.random_q50(N, K, 5700)
+    W5[:64] = 0
+    W5[64:128] = 0xFF
+    AS = np.full((M, K // 32), 0.5, np.float32)
+    WS = np.full((N, K // 32), 0.25, np.float32)
+    _check(A, AS, W5, WS, dev, "ring extreme")
+    for b, e in ((1, 110), (5, 126)):
+        WS[5:30, b] = np.float32(2.0 ** e)
+        AS[:, b] = np.float32(2.0 ** -e)
+    _check(A, AS, W5, WS, dev, "ring huge weight scales")
