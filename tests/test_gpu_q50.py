@@ -92,6 +92,10 @@ SHAPES = [
     # activation row
     (7, 4096, 2048), (2, 1, 32), (4, 14336, 4096), (5, 333, 2080), (2, 3000, 6144),
     (5, 1000, 8192), (3, 500, 14336), (2, 65, 16384), (6, 777, 14336), (7, 129, 16384),
+    # one row: rows of 4 to 288 blocks, one to several rows per wave group,
+    # a single weight row
+    (1, 1000, 128), (1, 333, 1536), (1, 777, 1664), (1, 5000, 3200), (1, 4096, 6272),
+    (1, 3000, 9216), (1, 1, 4096),
 ]
 
 
