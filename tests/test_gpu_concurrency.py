@@ -37,6 +37,7 @@ CASES = [
     ("qdot", 300, 2000, 1056, 3),
     ("qmma", 64, 1024, 4096, 1),
     ("q50", 1, 4096, 4096, None),
+    ("q50", 520, 2100, 1024, None),
     ("partials", 16, 512, 4096, 1),
     ("quantize", 512, 0, 4096, None),
 ]

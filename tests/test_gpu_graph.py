@@ -75,6 +75,28 @@ def test_qdot_graph_replay(dev, M, N, K):
     _replay_and_compare(g, C, eager, "q8_qdot %dx%dx%d path %d" % (M, N, K, q8.q8_qdot_path(M, N, K)))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (40, 7000, 1056), (520, 2100, 1024)])
+def test_q50_graph_replay(dev, M, N, K):
+    # Q5_0 weights: the matvec, the K-split GEMM and the ring GEMM
+    A, AS, _, WS = _case(M, N, K, 41 + M + N + K)
+    W5 = synth.random_q50(N, K, 42 + M)
+    tA, tAS, tW5, tWS = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (A, AS, W5, WS))
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    q8.q8_q50_qdot(tA, tAS, tW5, tWS, C)
+    torch.cuda.synchronize()
+    eager = C.cpu().numpy().copy()
+    out, mag = oracle.q50_qdot_f64(A, AS, W5, WS)
+    assert oracle.within_tolerance(eager, out, mag).all()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            q8.q8_q50_qdot(tA, tAS, tW5, tWS, C, stream=s)
+    torch.cuda.synchronize()
+    _replay_and_compare(g, C, eager, "q8_q50_qdot %dx%dx%d path %d" % (M, N, K, q8.q8_q50_path(M, N, K)))
+
+
 def test_partials_and_quantize_graph_replay(dev):
     M, N, K = 64, 300, 2048
     A, AS, W, WS = _case(M, N, K, 77)
