@@ -520,7 +520,14 @@ def main():
         ("qdot", synth.Workload(2, "q8_qgemm_m32_n4096_k14336_outliers", 32, 4096, 14336, True)),
         ("qdotws", synth.Workload(2, "q8_qgemm_m32_n4096_k14336_outliers", 32, 4096, 14336, True)),
     ]
-    late_variants = [] if (args.no_variants or args.profile) else [("qmma", synth.WORKLOADS[4])]
+    # Last, the GEMMs: qmma_t on the prompt workload, Q5_0 weights on it (the
+    # 64 x 64-tile ring GEMM, decoding in LDS), and a medium prompt
+    # projection on that kernel's two-workgroups-per-unit form.
+    late_variants = [] if (args.no_variants or args.profile) else [
+        ("qmma", synth.WORKLOADS[4]),
+        ("q50", synth.WORKLOADS[4]),
+        ("qdot", synth.Workload(4, "q8_qgemm_m512_n4096_k4096", 512, 4096, 4096, False)),
+    ]
     if variants or late_variants:
         result["variants"] = []
 
