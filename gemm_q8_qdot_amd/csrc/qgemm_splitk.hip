@@ -5,7 +5,8 @@
 // section "Quantized built-ins"), or qmma_t with the weight scales stored
 // [K/32][N] (same table): C[i, j] = sum_b AS[i, b] WS[j, b] P[i, j, b], with
 // P the exact int32 block sums ("Quantized built-ins and formats", section
-// "Q8_0": the inner sum is taken in integers).
+// "Q8_0": the inner sum is taken in integers); and the q50 rows of the same
+// table, W held as Q5_0 blocks (value = code - 16).
 //
 // Why: with a long contraction and few output tiles (M = 32, N = 4096,
 // K = 14336: 128 tiles of 32 x 32) the one-tile-per-workgroup GEMM walks
@@ -49,6 +50,10 @@
 //     left zero-filled for the next call.
 //   - The debug entry runs the same loads and MFMAs and stores each block
 //     sum (D - bias) where the epilogue would run; it needs no workspace.
+//   - Q5_0 weights (half-width form, one slice): each stage's raw 20-byte
+//     blocks are staged like the other operands and decoded once into a
+//     signed-byte tile laid out like the activation tile, behind a second
+//     barrier, before the same MFMA loop.
 #include "q8_device.h"
 #include "q8_launch.h"
 
