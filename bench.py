@@ -68,6 +68,8 @@ def parse():
                     help="only launch the headline kernel (for rocprofv3 counter passes)")
     ap.add_argument("--shape", default="", metavar="M,N,K",
                     help="with --profile: launch this shape instead (generators and seeds of --workload)")
+    ap.add_argument("--entry", default="qdot", choices=("qdot", "qmma", "q50"),
+                    help="with --profile: the entry to launch (q50: Q5_0 weights)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB 10 times and exit (counter calibration)")
     return ap.parse_args()
@@ -409,8 +411,10 @@ def main():
             sys.exit("bench.py: --shape is for --profile runs only (the headline is a listed workload)")
         M, N, K = (int(x) for x in args.shape.split(","))
         head_w = synth.Workload(head_w.index, "q8_shape_m%d_n%d_k%d" % (M, N, K), M, N, K, head_w.outliers)
+    if args.entry != "qdot" and not args.profile:
+        sys.exit("bench.py: --entry is for --profile runs only (the headline is q8_qdot)")
     log("[bench] preparing %s" % head_w.name)
-    head = Operands(torch, q8, head_w, rotate=not args.no_rotate)
+    head = Operands(torch, q8, head_w, rotate=not args.no_rotate, kind=args.entry)
     log("[bench] %s: %d rotated copies; timing %d steps after %d warmup"
         % (head_w.name, head.R, args.steps, args.warmup))
     ms, wall = time_launches(torch, q8, head, args.steps, args.warmup)
