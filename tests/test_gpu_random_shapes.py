@@ -5,7 +5,8 @@ reached several times with sizes nobody picked by hand: one activation row,
 small batches (2..7 rows), the K-split GEMM (few output tiles), the
 LDS-staged GEMM (M >= 128 and many tiles, short K) and the 64 x 64-tile GEMM
 over all of K (medium M x N, short K; and, two workgroups per compute unit,
-shapes the staged GEMM would take but is slower on); N and K/32 are
+shapes the staged GEMM would take but is slower on, and shapes past one
+round of its tiles, Q5_0 weights included); N and K/32 are
 ragged (any value; one activation row up to 600 blocks, past the 16 KiB
 rows of the one-row kernels).  Each case runs q8_qdot, q8_qmma (the same
 scales transposed), q8_q50_qdot and q8_q50_qmma (Q5_0 weights) and both
@@ -64,6 +65,14 @@ def _draw_cases(per_regime=6, seed=20261202):
         n_lo = 224 * (-(-128 // -(-M // 128)))
         n_hi = min(224 * (256 // -(-M // 128)), 64 * (1049 // -(-M // 64)))
         cases.append((M, int(rng.integers(n_lo, n_hi + 1)), 32 * int(rng.integers(1, 9))))
+    for _ in range(per_regime):       # 257..600 tiles of 64 x 64, too few staged
+        # tiles: the 64 x 64-tile GEMM, two workgroups per unit (Q5_0 weights
+        # too: K/32 a multiple of 4)
+        M = int(rng.integers(64, 601))
+        mt = -(-M // 64)
+        nt = int(rng.integers(-(-257 // mt), 600 // mt + 1))
+        N = 64 * nt - int(rng.integers(0, 64))
+        cases.append((M, N, 128))
     return cases
 
 
@@ -138,8 +147,9 @@ def test_cases_reach_every_path():
     # each regime of the draw lands on its dispatch path (0 matvec,
     # 1 K-split GEMM, 2 LDS-staged GEMM, 3 64 x 64-tile GEMM over all of K)
     paths = [q8.q8_qdot_path(M, N, K) for M, N, K in CASES]
-    per = len(CASES) // 6
+    per = len(CASES) // 7
     assert paths[:2 * per] == [0] * (2 * per)
     assert paths[2 * per:3 * per] == [1] * per
     assert paths[3 * per:4 * per] == [2] * per, CASES[3 * per:4 * per]
-    assert paths[4 * per:] == [3] * (2 * per), CASES[4 * per:]
+    assert paths[4 * per:] == [3] * (3 * per), CASES[4 * per:]
+    assert [q8.q8_q50_path(M, N, K) for M, N, K in CASES[6 * per:]] == [3] * per, CASES[6 * per:]
