@@ -45,6 +45,11 @@ VALU_LANE_OPS_PER_S = 256 * 4 * 32 * 2.4e9
 EPILOGUE_VALU_OPS = 2            # f32 VALU ops per (i, j, block) in the MFMA epilogue
 CACHE_DEFEAT_BYTES = 1 << 30     # rotate >= 1 GiB of distinct operand copies
 KERNEL_NAMES = ("matvec", "qgemm_ksplit", "qgemm_staged", "qgemm_splitk")              # by q8_qdot_path
+# Launches per timing window of the secondary figures (the other workloads,
+# the variants, the shard shares, the quantizer): at least 50, so that the
+# window's fixed cost (~1.5 us for the events and the first dispatch) stays
+# near 1 % of the small kernels' figures; the headline takes --steps.
+MIN_WINDOW = 50
 KERNEL_SOURCES = ("matvec.hip", "qgemm_ksplit.hip", "qgemm.hip", "qgemm_splitk.hip")   # their csrc files
 
 
@@ -470,7 +475,7 @@ def main():
     for idx in others:
         ow = synth.WORKLOADS[idx]
         ops = Operands(torch, q8, ow, rotate=not args.no_rotate)
-        ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
+        ms3, _ = time_launches(torch, q8, ops, max(MIN_WINDOW, args.steps // 4), max(3, args.warmup // 4))
         rec = {"workload": ow.name, "M": ow.M, "N": ow.N, "K": ow.K,
                "kernel": KERNEL_NAMES[q8.q8_qdot_path(ow.M, ow.N, ow.K)],
                "us_per_launch": round(ms3 * 1e3, 3),
@@ -497,7 +502,7 @@ def main():
         result["shard_share"] = []
     for split, full, sw_ in shares:
         ops = Operands(torch, q8, sw_, rotate=not args.no_rotate)
-        ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
+        ms3, _ = time_launches(torch, q8, ops, max(MIN_WINDOW, args.steps // 4), max(3, args.warmup // 4))
         rec = {"split": split, "of": full.name, "workload": sw_.name, "M": sw_.M, "N": sw_.N, "K": sw_.K,
                "kernel": KERNEL_NAMES[q8.q8_qdot_path(sw_.M, sw_.N, sw_.K)],
                "us_per_launch": round(ms3 * 1e3, 3),
@@ -538,7 +543,7 @@ def main():
     def time_variants(todo):
         for kind, vw in todo:
             ops = Operands(torch, q8, vw, rotate=not args.no_rotate, kind=kind)
-            ms3, _ = time_launches(torch, q8, ops, max(20, args.steps // 4), max(3, args.warmup // 4))
+            ms3, _ = time_launches(torch, q8, ops, max(MIN_WINDOW, args.steps // 4), max(3, args.warmup // 4))
             rec = {"entry": {"qdot": "q8_qdot", "qmma": "q8_qmma", "q50": "q8_q50_qdot",
                              "qdotws": "q8_qdot_ws"}[kind],
                    "workload": vw.name, "M": vw.M, "N": vw.N, "K": vw.K,
@@ -562,7 +567,7 @@ def main():
     if quant:
         result["quantize"] = []
     for rows, K in quant:
-        rec = time_quantize(torch, q8, rows, K, max(20, args.steps // 4), max(3, args.warmup // 4),
+        rec = time_quantize(torch, q8, rows, K, max(MIN_WINDOW, args.steps // 4), max(3, args.warmup // 4),
                             rotate=not args.no_rotate)
         result["quantize"].append(rec)
         log("[bench] q8_quantize %dx%d: %.3f us/launch, %.1f GB/s (%.1f%% HBM)"
